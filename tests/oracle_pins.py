@@ -1,0 +1,218 @@
+"""Checks that pin the CPU oracle to things other than itself.
+
+Each check takes the oracle module (or a stand-in with the same functions) so
+that the planted-mistake test can run the same checks against deliberately
+broken copies of it and confirm that every copy fails at least one check.
+
+What each check pins, and where the fact comes from:
+* brute_force: scalar pure-Python evaluation of the cross-entropy definition
+  (log of a sum of exponentials minus the target logit; gradient of the mean)
+  on tiny random instances, without the max shift the oracle uses.
+* torch_reference: torch's float64 cross_entropy + autograd on the CPU.
+* finite_differences: central differences of the mean loss in every entry of
+  X and W; independent of any gradient formula.
+* zero_weight: W = 0 makes every logit 0, so each valid token's loss is ln V,
+  dX = 0, and dW_v = g (sum of valid x_i / V - sum of valid x_i with t_i = v).
+* logistic: V = 2 reduces to the logistic loss log(1 + exp(y_other - y_t)).
+* invariants: softmax-minus-one-hot rows sum to 0 (so sum_v dW_v = 0);
+  adding one vector c to every vocabulary row leaves loss and gradients
+  unchanged; an ignored row contributes nothing (equal to dropping it while
+  keeping n_valid); mean * n_valid = sum; the pages' ring fold over any shard
+  order and any shard count equals the plain definition.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def rand_instance(rng, n, h, v, ignore=0, scale=1.0):
+    x = rng.standard_normal((n, h)) * scale
+    w = rng.standard_normal((v, h)) * scale
+    t = rng.integers(0, v, size=n)
+    if ignore:
+        t[rng.choice(n, size=ignore, replace=False)] = -100
+    return x, w, t
+
+
+def _brute(x, w, t, ignore_index=-100):
+    n, h = x.shape
+    v = w.shape[0]
+    valid = [int(t[i]) != ignore_index for i in range(n)]
+    n_valid = sum(valid)
+    z = [[math.fsum(x[i][k] * w[j][k] for k in range(h)) for j in range(v)] for i in range(n)]
+    tok = []
+    lse = []
+    for i in range(n):
+        s = math.log(math.fsum(math.exp(zz) for zz in z[i]))
+        lse.append(s)
+        tok.append(s - z[i][int(t[i])] if valid[i] else 0.0)
+    loss = math.fsum(tok) / n_valid
+    dx = [[0.0] * h for _ in range(n)]
+    dw = [[0.0] * h for _ in range(v)]
+    for i in range(n):
+        if not valid[i]:
+            continue
+        den = math.fsum(math.exp(zz) for zz in z[i])
+        for j in range(v):
+            gij = (math.exp(z[i][j]) / den - (1.0 if j == int(t[i]) else 0.0)) / n_valid
+            for k in range(h):
+                dx[i][k] += gij * w[j][k]
+                dw[j][k] += gij * x[i][k]
+    return loss, np.array(tok), np.array(lse), np.array(dx), np.array(dw)
+
+
+def check_brute_force(orc, seeds=range(6)):
+    for seed in seeds:
+        rng = np.random.default_rng(1000 + seed)
+        n, h, v = 1 + seed % 7, 1 + (seed * 3) % 8, 2 + (seed * 5) % 31
+        x, w, t = rand_instance(rng, n, h, v, ignore=(n - 1) // 3)
+        loss, tok, lse, dx, dw = _brute(x, w, t)
+        for rb in (None, 1, 2):
+            r = orc.cross_entropy(x, w, t, row_block=rb)
+            assert abs(r.loss - loss) <= 1e-12 * max(1.0, abs(loss)), (seed, rb, r.loss, loss)
+            np.testing.assert_allclose(r.token_loss, tok, rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(r.lse, lse, rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(r.d_hidden, dx, rtol=1e-10, atol=1e-13)
+            np.testing.assert_allclose(r.d_weight, dw, rtol=1e-10, atol=1e-13)
+
+
+def check_torch_reference(orc, x, w, t, tol=1e-10, row_block=None):
+    import torch
+    xt = torch.tensor(x, dtype=torch.float64, requires_grad=True)
+    wt = torch.tensor(w, dtype=torch.float64, requires_grad=True)
+    tt = torch.tensor(np.asarray(t, dtype=np.int64))
+    logits = xt @ wt.T
+    loss = torch.nn.functional.cross_entropy(logits, tt, ignore_index=-100, reduction="mean")
+    loss.backward()
+    tok = torch.nn.functional.cross_entropy(logits.detach(), tt, ignore_index=-100, reduction="none")
+    r = orc.cross_entropy(x, w, t, row_block=row_block)
+    assert abs(r.loss - loss.item()) <= tol * max(1.0, abs(loss.item())), (r.loss, loss.item())
+    np.testing.assert_allclose(r.token_loss, tok.numpy(), rtol=tol, atol=tol)
+    np.testing.assert_allclose(r.lse, torch.logsumexp(logits.detach(), dim=1).numpy(), rtol=tol, atol=tol)
+    gx, gw = xt.grad.numpy(), wt.grad.numpy()
+    assert np.max(np.abs(r.d_hidden - gx)) <= tol * max(1e-30, np.max(np.abs(gx)))
+    assert np.max(np.abs(r.d_weight - gw)) <= tol * max(1e-30, np.max(np.abs(gw)))
+
+
+def check_finite_differences(orc, seed=7):
+    rng = np.random.default_rng(seed)
+    x, w, t = rand_instance(rng, 5, 3, 6, ignore=1)
+    r = orc.cross_entropy(x, w, t)
+
+    def loss_at(xx, ww):
+        return orc.cross_entropy(xx, ww, t, grad=False).loss
+
+    for arr, grad in ((x, r.d_hidden), (w, r.d_weight)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            hstep = 1e-6 * max(1.0, abs(arr[idx]))
+            old = arr[idx]
+            arr[idx] = old + hstep
+            lp = loss_at(x, w)
+            arr[idx] = old - hstep
+            lm = loss_at(x, w)
+            arr[idx] = old
+            num[idx] = (lp - lm) / (2 * hstep)
+        err = np.max(np.abs(num - grad)) / max(1e-30, np.max(np.abs(grad)))
+        assert err <= 1e-6, err
+
+
+def check_zero_weight(orc, seed=3):
+    rng = np.random.default_rng(seed)
+    n, h, v = 9, 4, 11
+    x = rng.standard_normal((n, h))
+    t = rng.integers(0, v, size=n)
+    t[[2, 5]] = -100
+    w = np.zeros((v, h))
+    r = orc.cross_entropy(x, w, t)
+    assert abs(r.loss - math.log(v)) <= 1e-14, r.loss
+    valid = t != -100
+    np.testing.assert_allclose(r.token_loss[valid], math.log(v), rtol=0, atol=1e-14)
+    assert np.all(r.d_hidden == 0.0)
+    g = 1.0 / valid.sum()
+    expect = np.zeros((v, h))
+    xs = x[valid].sum(axis=0)
+    for j in range(v):
+        expect[j] = g * (xs / v - x[valid & (t == j)].sum(axis=0))
+    np.testing.assert_allclose(r.d_weight, expect, rtol=1e-12, atol=1e-15)
+
+
+def check_logistic(orc, seed=4):
+    rng = np.random.default_rng(seed)
+    x, w, t = rand_instance(rng, 8, 5, 2)
+    r = orc.cross_entropy(x, w, t)
+    z = x @ w.T
+    for i in range(8):
+        other = 1 - int(t[i])
+        expect = math.log1p(math.exp(z[i, other] - z[i, int(t[i])]))
+        assert abs(r.token_loss[i] - expect) <= 1e-13 * max(1.0, expect)
+
+
+def check_invariants(orc, seed=5):
+    rng = np.random.default_rng(seed)
+    n, h, v = 12, 6, 24
+    x, w, t = rand_instance(rng, n, h, v, ignore=3)
+    base = orc.cross_entropy(x, w, t)
+    # rows of softmax - onehot sum to zero, so the vocabulary rows of dW sum to zero
+    assert np.max(np.abs(base.d_weight.sum(axis=0))) <= 1e-14 * max(1.0, np.max(np.abs(base.d_weight)) * v)
+    # a constant vector added to every vocabulary row shifts each row's logits uniformly
+    c = rng.standard_normal(h)
+    sh = orc.cross_entropy(x, w + c[None, :], t)
+    assert abs(sh.loss - base.loss) <= 1e-12
+    np.testing.assert_allclose(sh.d_hidden, base.d_hidden, atol=1e-13)
+    np.testing.assert_allclose(sh.d_weight, base.d_weight, atol=1e-13)
+    # ignored rows: zero loss, zero dX row, and the same as dropping them (same n_valid)
+    ign = t == -100
+    assert np.all(base.token_loss[ign] == 0.0) and np.all(base.d_hidden[ign] == 0.0)
+    kept = orc.cross_entropy(x[~ign], w, t[~ign])
+    assert abs(kept.loss - base.loss) <= 1e-13
+    np.testing.assert_allclose(kept.d_hidden, base.d_hidden[~ign], atol=1e-14)
+    np.testing.assert_allclose(kept.d_weight, base.d_weight, atol=1e-14)
+    # mean * n_valid = sum, and "sum" gradients are n_valid times the mean ones
+    sm = orc.cross_entropy(x, w, t, reduction="sum")
+    assert abs(sm.loss - base.loss * base.n_valid) <= 1e-12 * abs(sm.loss)
+    np.testing.assert_allclose(sm.d_hidden, base.d_hidden * base.n_valid, rtol=1e-12, atol=1e-14)
+    # a row's loss does not depend on the other rows
+    perm = rng.permutation(n)
+    pr = orc.cross_entropy(x[perm], w, t[perm])
+    np.testing.assert_allclose(pr.token_loss, base.token_loss[perm], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(pr.d_hidden, base.d_hidden[perm], rtol=1e-12, atol=1e-15)
+    # the pages' per-round fold gives the same result for every shard count and order
+    for p_count in (1, 2, 3, 4, 6, 8, 12, 24):
+        vs = v // p_count
+        shards = [w[s * vs:(s + 1) * vs] for s in range(p_count)]
+        for order in (list(range(p_count)), [(-k) % p_count for k in range(p_count)],
+                      list(rng.permutation(p_count))):
+            rf = orc.ring_fold(x, shards, order, t)
+            assert abs(rf.loss - base.loss) <= 1e-12 * max(1.0, abs(base.loss))
+            np.testing.assert_allclose(rf.token_loss, base.token_loss, rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(rf.lse, base.lse, rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(rf.d_hidden, base.d_hidden, rtol=1e-10, atol=1e-14)
+            np.testing.assert_allclose(rf.d_weight, base.d_weight, rtol=1e-10, atol=1e-14)
+
+
+def check_row_samples(orc, seed=6):
+    rng = np.random.default_rng(seed)
+    x, w, t = rand_instance(rng, 10, 4, 9, ignore=2)
+    base = orc.cross_entropy(x, w, t)
+    g = np.where(t != -100, 1.0 / base.n_valid, 0.0)
+    rows = np.array([0, 3, 7, 9])
+    lse, tok, dx = orc.token_rows(x[rows], w, t[rows], g[rows])
+    np.testing.assert_allclose(lse, base.lse[rows], rtol=1e-13)
+    np.testing.assert_allclose(tok, base.token_loss[rows], rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(dx, base.d_hidden[rows], rtol=1e-12, atol=1e-15)
+
+
+def all_small_checks(orc):
+    """Every pin that runs in well under a second (used by the planted-mistake test)."""
+    check_brute_force(orc)
+    rng = np.random.default_rng(11)
+    x, w, t = rand_instance(rng, 16, 8, 40, ignore=4)
+    check_torch_reference(orc, x, w, t, row_block=5)
+    check_finite_differences(orc)
+    check_zero_weight(orc)
+    check_logistic(orc)
+    check_invariants(orc)
+    check_row_samples(orc)
