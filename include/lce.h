@@ -1,0 +1,133 @@
+/*
+ * lce.h - memory-bounded vocabulary projection + cross-entropy on MI355X (C ABI).
+ *
+ * Computes the exact cross-entropy of the logits X W^T, where the vocabulary
+ * weight W (V x H) arrives as P column shards (contiguous vocabulary
+ * intervals of V/P ids), and its gradients, without ever forming the N x V
+ * logit tensor. This is one rank's share of the ring data-tensor-parallel
+ * vocabulary projection described in "Flattening Every Memory Peak in
+ * Long-Context Mixture-of-Experts Training", section 3.2 (Ring-DTP): the
+ * rank's own batch meets every shard once, in the order a ring delivers them,
+ * and each meeting folds the logits into a per-token running maximum and
+ * exponential sum (the online-softmax update, Eq. 3 of that section); the
+ * negative log-likelihood is m + log z - y_t. Backward recomputes each logit
+ * block from the saved normalizer lse = m + log z. The same page requires the
+ * operator to return the forward values and gradients of the plain
+ * implementation, changing only the order of computation.
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers marked "device" are HIP device pointers; "host" pointers are
+ *    read before the call returns. The caller owns and frees every buffer,
+ *    including the workspace; the library never allocates device memory and
+ *    never synchronizes the stream.
+ *  - All work is enqueued on `stream` (a hipStream_t; NULL = default stream).
+ *    Results are valid once the stream reaches the enqueued work.
+ *  - Every argument check runs on the host before any GPU work is enqueued;
+ *    a failed check returns a negative status and enqueues nothing.
+ *  - Layouts: hidden bf16 [N][H] row-major; shard s bf16 [V/P][H] row-major,
+ *    holding vocabulary ids [s*V/P, (s+1)*V/P); targets int32 [N].
+ *    bf16 is passed as raw 16-bit patterns.
+ *  - Alignment: every device pointer must be 16-byte aligned. H must be a
+ *    positive multiple of 64.
+ *  - Limits: N*H, (V/P)*H and N*(V/P) below 2^31 elements; 1 <= P <= 256.
+ *  - Calls are thread-safe; concurrent calls need distinct workspaces.
+ */
+#ifndef LCE_H
+#define LCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#ifndef LCE_API
+#define LCE_API __attribute__((visibility("default")))
+#endif
+
+#define LCE_OK 0
+#define LCE_ERR_INVALID_ARG (-1) /* null pointer, bad size, order not a permutation */
+#define LCE_ERR_UNSUPPORTED (-2) /* H not a multiple of 64, misaligned pointer, size limit */
+#define LCE_ERR_WORKSPACE (-3)   /* workspace smaller than lce_workspace_bytes() */
+#define LCE_ERR_HIP (-4)         /* a HIP launch failed; see lce_last_error() */
+
+#define LCE_REDUCTION_MEAN 0 /* mean over tokens whose target != ignore_index */
+#define LCE_REDUCTION_SUM 1  /* sum over tokens whose target != ignore_index */
+
+#define LCE_MAX_SHARDS 256
+
+typedef struct lce_dims {
+  int64_t n_tokens;     /* N >= 1 */
+  int64_t hidden;       /* H >= 64, multiple of 64 */
+  int64_t vocab;        /* V >= 1, divisible by n_shards */
+  int32_t n_shards;     /* P, 1..LCE_MAX_SHARDS */
+  int32_t ignore_index; /* targets equal to this are skipped (e.g. -100) */
+  int32_t reduction;    /* LCE_REDUCTION_MEAN or LCE_REDUCTION_SUM */
+  int32_t reserved;     /* must be 0 */
+} lce_dims;
+
+/*
+ * Bytes of device workspace lce_forward and lce_backward need for `dims`.
+ * Pure host function. The size grows with N and H and is bounded independently
+ * of V: it holds per-token state (O(N)), a transposed copy of the hidden states
+ * (N*H bf16) and fixed-size gradient chunks, never a logit strip.
+ * Returns 0 if dims is invalid.
+ */
+LCE_API size_t lce_workspace_bytes(const lce_dims* dims);
+
+/*
+ * Forward: loss and the saved normalizer.
+ *  hidden       device bf16 [N][H]
+ *  w_shards     host array of P device pointers, each bf16 [V/P][H]
+ *  shard_order  host int32 [P], a permutation of 0..P-1: round k meets shard
+ *               shard_order[k]. NULL = the ring order of rank 0, k -> (P-k) % P.
+ *               The result does not depend on the order except for fp32
+ *               rounding.
+ *  targets      device int32 [N]; ids in [0, V) or ignore_index. An id outside
+ *               [0, V) that is not ignore_index makes that token's loss NaN
+ *               (and so the mean); no host synchronization is done to detect it.
+ *  loss         device fp32 scalar, written: mean (or sum) over non-ignored
+ *               tokens; NaN for a mean over zero tokens.
+ *  lse          device fp32 [N], written: log-sum-exp of each token's full
+ *               logit row (every token, ignored ones included). Keep it for
+ *               lce_backward: it is the only state backward needs.
+ *  token_loss   device fp32 [N] or NULL; written: lse - target logit, 0 for
+ *               ignored tokens.
+ *  workspace    device buffer of at least lce_workspace_bytes(dims) bytes.
+ */
+LCE_API int lce_forward(const lce_dims* dims, const void* hidden, const void* const* w_shards, const int32_t* shard_order,
+                const int32_t* targets, float* loss, float* lse, float* token_loss, void* workspace,
+                size_t workspace_bytes, void* stream);
+
+/*
+ * Backward: gradients of the (mean or sum) loss, recomputed shard by shard
+ * from the saved normalizer.
+ *  hidden, w_shards, shard_order, targets   as for lce_forward
+ *  lse          device fp32 [N] from lce_forward on the same inputs
+ *  dloss        device fp32 scalar: d(objective)/d(loss)
+ *  d_hidden     device fp32 [N][H], overwritten with dloss * dL/dX.
+ *               Rows of ignored tokens are exactly 0.
+ *  d_w_shards   host array of P device pointers, each fp32 [V/P][H],
+ *               overwritten with dloss * dL/dW for that shard.
+ *  workspace    as for lce_forward (the forward's contents are not needed).
+ * A target outside [0, V) that is not ignore_index makes every output NaN.
+ */
+LCE_API int lce_backward(const lce_dims* dims, const void* hidden, const void* const* w_shards, const int32_t* shard_order,
+                 const int32_t* targets, const float* lse, const float* dloss, float* d_hidden,
+                 float* const* d_w_shards, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static text for a status code. */
+LCE_API const char* lce_status_string(int status);
+
+/* Text of the last failure on the calling thread ("" if none). */
+LCE_API const char* lce_last_error(void);
+
+/* ABI version: (major << 16) | minor. */
+LCE_API int lce_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LCE_H */

@@ -1,0 +1,170 @@
+"""Memory-bounded vocabulary projection + cross-entropy for MI355X (gfx950).
+
+Thin Python binding over the C-ABI library ``liblce.so`` (see include/lce.h).
+Every step of the computation runs in the library's HIP kernels; this module
+only marshals arguments: torch supplies device memory, data pointers and the
+current stream. There is no fallback path: if the library is missing or no
+GPU is present, the compute functions raise.
+
+    loss, lse = forward(hidden, shards, targets)
+    d_hidden, d_shards = backward(hidden, shards, targets, lse, dloss)
+
+hidden: bf16 [N][H] cuda tensor; shards: list of P bf16 [V/P][H] cuda tensors
+(shard s holds vocabulary ids [s*V/P, (s+1)*V/P)); targets: int32 [N].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence, Tuple
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblce.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+REDUCTIONS = {"mean": 0, "sum": 1}
+EXPORTED = ("lce_workspace_bytes", "lce_forward", "lce_backward", "lce_status_string",
+            "lce_last_error", "lce_version")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("n_tokens", ctypes.c_int64), ("hidden", ctypes.c_int64), ("vocab", ctypes.c_int64),
+                ("n_shards", ctypes.c_int32), ("ignore_index", ctypes.c_int32),
+                ("reduction", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class LceError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"lce status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load liblce.so (after torch, so both share one HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m memory_bounded_vocabulary_amd.build`")
+    import torch  # noqa: F401  (loads the HIP runtime the library binds to)
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32p, f32p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_float)
+    dimp = ctypes.POINTER(Dims)
+    L.lce_workspace_bytes.argtypes = [dimp]
+    L.lce_workspace_bytes.restype = ctypes.c_size_t
+    L.lce_forward.argtypes = [dimp, vp, ctypes.POINTER(vp), i32p, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.lce_forward.restype = ctypes.c_int
+    L.lce_backward.argtypes = [dimp, vp, ctypes.POINTER(vp), i32p, vp, vp, vp, vp, ctypes.POINTER(vp), vp,
+                               ctypes.c_size_t, vp]
+    L.lce_backward.restype = ctypes.c_int
+    L.lce_status_string.argtypes = [ctypes.c_int]
+    L.lce_status_string.restype = ctypes.c_char_p
+    L.lce_last_error.argtypes = []
+    L.lce_last_error.restype = ctypes.c_char_p
+    L.lce_version.argtypes = []
+    L.lce_version.restype = ctypes.c_int
+    del f32p
+    _lib = L
+    return L
+
+
+def make_dims(n_tokens: int, hidden: int, vocab: int, n_shards: int, ignore_index: int = -100,
+              reduction: str = "mean") -> Dims:
+    return Dims(n_tokens, hidden, vocab, n_shards, ignore_index, REDUCTIONS[reduction], 0)
+
+
+def workspace_bytes(n_tokens: int, hidden: int, vocab: int, n_shards: int, ignore_index: int = -100,
+                    reduction: str = "mean") -> int:
+    d = make_dims(n_tokens, hidden, vocab, n_shards, ignore_index, reduction)
+    return int(lib().lce_workspace_bytes(ctypes.byref(d)))
+
+
+def _check(status: int) -> None:
+    if status != OK:
+        L = lib()
+        raise LceError(status, f"{L.lce_status_string(status).decode()}: {L.lce_last_error().decode()}")
+
+
+def _ptr_array(ptrs: Sequence[int]):
+    return (ctypes.c_void_p * len(ptrs))(*ptrs)
+
+
+def _order_array(order: Optional[Sequence[int]]):
+    if order is None:
+        return None
+    return (ctypes.c_int32 * len(order))(*[int(o) for o in order])
+
+
+def _stream(stream) -> int:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def _require_cuda(*tensors) -> None:
+    for t in tensors:
+        if not t.is_cuda:
+            raise ValueError("lce runs on the GPU only: every tensor must be a cuda tensor")
+
+
+def alloc_workspace(n_tokens: int, hidden: int, vocab: int, n_shards: int, device=None, ignore_index: int = -100,
+                    reduction: str = "mean"):
+    import torch
+    nbytes = workspace_bytes(n_tokens, hidden, vocab, n_shards, ignore_index, reduction)
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device or "cuda")
+
+
+def forward(hidden, shards: Sequence, targets, ignore_index: int = -100, order: Optional[Sequence[int]] = None,
+            reduction: str = "mean", workspace=None, token_loss: bool = False, stream=None):
+    """Loss and saved normalizer; returns (loss, lse) or (loss, lse, token_loss)."""
+    import torch
+    _require_cuda(hidden, targets, *shards)
+    n, h = hidden.shape
+    p = len(shards)
+    v = p * shards[0].shape[0]
+    d = make_dims(n, h, v, p, ignore_index, reduction)
+    if workspace is None:
+        workspace = alloc_workspace(n, h, v, p, hidden.device, ignore_index, reduction)
+    loss = torch.empty((), dtype=torch.float32, device=hidden.device)
+    lse = torch.empty(n, dtype=torch.float32, device=hidden.device)
+    tl = torch.empty(n, dtype=torch.float32, device=hidden.device) if token_loss else None
+    st = lib().lce_forward(ctypes.byref(d), hidden.data_ptr(), _ptr_array([s.data_ptr() for s in shards]),
+                           _order_array(order), targets.data_ptr(), loss.data_ptr(), lse.data_ptr(),
+                           tl.data_ptr() if tl is not None else None, workspace.data_ptr(),
+                           workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st)
+    return (loss, lse, tl) if token_loss else (loss, lse)
+
+
+def backward(hidden, shards: Sequence, targets, lse, dloss, ignore_index: int = -100,
+             order: Optional[Sequence[int]] = None, reduction: str = "mean", workspace=None,
+             d_hidden=None, d_shards: Optional[List] = None, stream=None) -> Tuple[object, List]:
+    """Gradients (d_hidden fp32 [N][H], [d_shard fp32 [V/P][H]]) of dloss * loss."""
+    import torch
+    _require_cuda(hidden, targets, lse, *shards)
+    n, h = hidden.shape
+    p = len(shards)
+    vs = shards[0].shape[0]
+    d = make_dims(n, h, p * vs, p, ignore_index, reduction)
+    if workspace is None:
+        workspace = alloc_workspace(n, h, p * vs, p, hidden.device, ignore_index, reduction)
+    if not torch.is_tensor(dloss):
+        dloss = torch.tensor(float(dloss), dtype=torch.float32, device=hidden.device)
+    if d_hidden is None:
+        d_hidden = torch.empty((n, h), dtype=torch.float32, device=hidden.device)
+    if d_shards is None:
+        d_shards = [torch.empty((vs, h), dtype=torch.float32, device=hidden.device) for _ in range(p)]
+    st = lib().lce_backward(ctypes.byref(d), hidden.data_ptr(), _ptr_array([s.data_ptr() for s in shards]),
+                            _order_array(order), targets.data_ptr(), lse.data_ptr(), dloss.data_ptr(),
+                            d_hidden.data_ptr(), _ptr_array([g.data_ptr() for g in d_shards]),
+                            workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st)
+    return d_hidden, d_shards
+
+
+def version() -> Tuple[int, int]:
+    v = lib().lce_version()
+    return v >> 16, v & 0xFFFF

@@ -1,0 +1,61 @@
+// CDNA4 (gfx950) device helpers: bf16 MFMA fragments, direct global->LDS
+// loads, wait counters and bf16 rounding. Device code only.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lce {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+#define LCE_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Finite stand-in for -infinity in the running maximum: (-FLT_MAX) - (-FLT_MAX)
+// is 0, never NaN, and exp2 of anything below it underflows to 0.
+constexpr float kNegBig = -3.4028234663852886e38f;
+
+__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// 32x32x16 bf16 MFMA: D = A * B + C. Lane l supplies A[l%32][k-group l/32] and
+// B[k-group l/32][l%32] (8 bf16 each); D element r of lane l sits at
+// row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16-byte global -> LDS copy issued by a whole wave: lane l's 16 bytes land at
+// lds_wave_base + 16*l. lds_wave_base must be wave-uniform.
+__device__ __forceinline__ void g2lds16(const void* gsrc, LCE_LDS void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, lds_wave_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// fp32 -> bf16, round to nearest even (hardware conversion on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, b);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Online log-sum-exp state in the log2 domain: (m, z) stands for 2^m * z.
+__device__ __forceinline__ void lse_merge(float& m, float& z, float m2, float z2) {
+  float mn = fmaxf(m, m2);
+  z = z * fast_exp2(m - mn) + z2 * fast_exp2(m2 - mn);
+  m = mn;
+}
+
+}  // namespace lce

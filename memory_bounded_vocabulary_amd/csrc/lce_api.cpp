@@ -1,0 +1,302 @@
+// C ABI of the memory-bounded vocabulary projection + cross-entropy: argument
+// checks, workspace layout and the host-side schedule of kernel launches.
+//
+// Schedule (one rank's share of "Flattening Every Memory Peak in Long-Context
+// Mixture-of-Experts Training", section 3.2, Ring-DTP):
+//   forward   target logits; round k = 0..P-1 folds shard order[k] into the
+//             per-token running (m, z); finalize lse = m + log z, the token
+//             losses and the loss.
+//   backward  g = dloss / n_valid; X^T once; then for every shard in ring
+//             order and every (vocabulary chunk, token chunk): recompute the
+//             logit block from lse and form G in bf16, then dX += G W_chunk and
+//             dW_chunk += G^T X_chunk (fp32).
+// Transient device memory is O(N) plus fixed-size chunks: no logit strip
+// (N x V/P) is ever formed.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/lce.h"
+#include "lce_internal.hpp"
+
+namespace {
+
+constexpr int64_t kTile = 256;
+constexpr int64_t kVocabChunkMax = 8192;   // vocabulary rows per backward chunk
+constexpr int64_t kTokenChunkMax = 16384;  // tokens per backward chunk
+constexpr int kMaxSplits = 16;             // forward vocabulary splits per shard
+constexpr int kTargetWorkgroups = 256;     // one per compute unit
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Plan {
+  int64_t N, H, V, P, Vs;
+  int64_t n_pad, row_blocks, col_tiles;
+  int64_t splits, tiles_per_split;
+  int64_t vs_pad, vcs, ncs;
+  // forward workspace
+  size_t off_state, off_yt, off_part, off_nvalid, fwd_bytes;
+  // backward workspace
+  size_t off_gscale, off_xt, off_wt, off_g, off_gt, bwd_bytes;
+  size_t bytes;
+};
+
+int check_dims(const lce_dims* d) {
+  if (!d) return fail(LCE_ERR_INVALID_ARG, "dims is NULL");
+  if (d->n_tokens < 1) return fail(LCE_ERR_INVALID_ARG, "n_tokens must be >= 1 (got %lld)", (long long)d->n_tokens);
+  if (d->hidden < 1) return fail(LCE_ERR_INVALID_ARG, "hidden must be >= 1 (got %lld)", (long long)d->hidden);
+  if (d->vocab < 1) return fail(LCE_ERR_INVALID_ARG, "vocab must be >= 1 (got %lld)", (long long)d->vocab);
+  if (d->n_shards < 1 || d->n_shards > LCE_MAX_SHARDS)
+    return fail(LCE_ERR_INVALID_ARG, "n_shards must be in [1, %d] (got %d)", LCE_MAX_SHARDS, d->n_shards);
+  if (d->vocab % d->n_shards)
+    return fail(LCE_ERR_INVALID_ARG, "vocab (%lld) is not divisible by n_shards (%d)", (long long)d->vocab,
+                d->n_shards);
+  if (d->reduction != LCE_REDUCTION_MEAN && d->reduction != LCE_REDUCTION_SUM)
+    return fail(LCE_ERR_INVALID_ARG, "reduction must be LCE_REDUCTION_MEAN or LCE_REDUCTION_SUM (got %d)",
+                d->reduction);
+  if (d->reserved != 0) return fail(LCE_ERR_INVALID_ARG, "reserved must be 0");
+  if (d->hidden % 64) return fail(LCE_ERR_UNSUPPORTED, "hidden (%lld) must be a multiple of 64", (long long)d->hidden);
+  const int64_t vs = d->vocab / d->n_shards;
+  const int64_t lim = int64_t(1) << 31;
+  const int64_t n_pad = round_up(d->n_tokens, kTile);
+  if (n_pad * d->hidden >= lim || round_up(vs, kTile) * d->hidden >= lim || n_pad * vs >= lim)
+    return fail(LCE_ERR_UNSUPPORTED, "sizes exceed 2^31 elements (N=%lld H=%lld V/P=%lld)",
+                (long long)d->n_tokens, (long long)d->hidden, (long long)vs);
+  return LCE_OK;
+}
+
+Plan make_plan(const lce_dims* d) {
+  Plan p{};
+  p.N = d->n_tokens;
+  p.H = d->hidden;
+  p.V = d->vocab;
+  p.P = d->n_shards;
+  p.Vs = p.V / p.P;
+  p.n_pad = round_up(p.N, kTile);
+  p.row_blocks = p.n_pad / kTile;
+  p.col_tiles = ceil_div(p.Vs, kTile);
+  // Split each shard's columns until the grid has about one workgroup per CU.
+  int64_t s = std::min<int64_t>({kMaxSplits, p.col_tiles, std::max<int64_t>(1, ceil_div(kTargetWorkgroups, p.row_blocks))});
+  p.tiles_per_split = ceil_div(p.col_tiles, s);
+  p.splits = ceil_div(p.col_tiles, p.tiles_per_split);
+  // Backward chunks: balanced, tile-aligned, bounded by constants.
+  p.vs_pad = round_up(p.Vs, kTile);
+  p.vcs = round_up(ceil_div(p.vs_pad, ceil_div(p.vs_pad, kVocabChunkMax)), kTile);
+  p.ncs = round_up(ceil_div(p.n_pad, ceil_div(p.n_pad, kTokenChunkMax)), kTile);
+
+  size_t o = 0;
+  p.off_state = o;
+  o = align256(o + size_t(p.splits) * p.n_pad * 8);
+  p.off_yt = o;
+  o = align256(o + size_t(p.n_pad) * 4);
+  p.off_part = o;
+  o = align256(o + size_t(p.row_blocks) * 16);
+  p.off_nvalid = o;
+  o = align256(o + 16);
+  p.fwd_bytes = o;
+
+  o = 0;
+  p.off_gscale = o;
+  o = align256(o + 16);
+  p.off_xt = o;
+  o = align256(o + size_t(p.H) * p.n_pad * 2);
+  p.off_wt = o;
+  o = align256(o + size_t(p.H) * p.vcs * 2);
+  p.off_g = o;
+  o = align256(o + size_t(p.ncs) * p.vcs * 2);
+  p.off_gt = o;
+  o = align256(o + size_t(p.vcs) * p.ncs * 2);
+  p.bwd_bytes = o;
+  p.bytes = std::max(p.fwd_bytes, p.bwd_bytes);
+  return p;
+}
+
+int check_order(const int32_t* order, int P, int32_t* out) {
+  if (!order) {
+    for (int k = 0; k < P; ++k) out[k] = (P - k) % P;
+    return LCE_OK;
+  }
+  bool seen[LCE_MAX_SHARDS] = {};
+  for (int k = 0; k < P; ++k) {
+    const int s = order[k];
+    if (s < 0 || s >= P || seen[s])
+      return fail(LCE_ERR_INVALID_ARG, "shard_order is not a permutation of 0..%d (entry %d = %d)", P - 1, k, s);
+    seen[s] = true;
+    out[k] = s;
+  }
+  return LCE_OK;
+}
+
+int check_common(const lce_dims* d, const void* hidden, const void* const* w_shards, const int32_t* targets,
+                 void* workspace, size_t workspace_bytes, Plan* plan) {
+  int st = check_dims(d);
+  if (st) return st;
+  if (!hidden || !w_shards || !targets) return fail(LCE_ERR_INVALID_ARG, "hidden, w_shards and targets must be non-NULL");
+  for (int s = 0; s < d->n_shards; ++s) {
+    if (!w_shards[s]) return fail(LCE_ERR_INVALID_ARG, "w_shards[%d] is NULL", s);
+    if (!aligned16(w_shards[s])) return fail(LCE_ERR_UNSUPPORTED, "w_shards[%d] is not 16-byte aligned", s);
+  }
+  if (!aligned16(hidden) || !aligned16(targets)) return fail(LCE_ERR_UNSUPPORTED, "hidden/targets not 16-byte aligned");
+  *plan = make_plan(d);
+  if (!workspace) return fail(LCE_ERR_INVALID_ARG, "workspace is NULL");
+  if (!aligned16(workspace)) return fail(LCE_ERR_UNSUPPORTED, "workspace is not 16-byte aligned");
+  if (workspace_bytes < plan->bytes)
+    return fail(LCE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, plan->bytes);
+  return LCE_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return LCE_OK;
+  return fail(LCE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t lce_workspace_bytes(const lce_dims* dims) {
+  if (check_dims(dims) != LCE_OK) return 0;
+  return make_plan(dims).bytes;
+}
+
+int lce_forward(const lce_dims* d, const void* hidden, const void* const* w_shards, const int32_t* shard_order,
+                const int32_t* targets, float* loss, float* lse, float* token_loss, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  Plan p;
+  int st = check_common(d, hidden, w_shards, targets, workspace, workspace_bytes, &p);
+  if (st) return st;
+  if (!loss || !lse) return fail(LCE_ERR_INVALID_ARG, "loss and lse must be non-NULL");
+  if (!aligned16(lse) || (token_loss && !aligned16(token_loss)))
+    return fail(LCE_ERR_UNSUPPORTED, "lse/token_loss not 16-byte aligned");
+  int32_t order[LCE_MAX_SHARDS];
+  st = check_order(shard_order, d->n_shards, order);
+  if (st) return st;
+  g_last_error.clear();
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float2* state = reinterpret_cast<float2*>(ws + p.off_state);
+  float* yt = reinterpret_cast<float*>(ws + p.off_yt);
+  double2* part = reinterpret_cast<double2*>(ws + p.off_part);
+  float* nvalid = reinterpret_cast<float*>(ws + p.off_nvalid);
+  const uint16_t* X = static_cast<const uint16_t*>(hidden);
+  const int N = int(p.N), H = int(p.H), Vs = int(p.Vs), V = int(p.V);
+
+  lce::ShardTable table{};
+  for (int k = 0; k < d->n_shards; ++k) table.p[k] = static_cast<const uint16_t*>(w_shards[k]);
+  st = hip_status(lce::launch_target_logit(X, N, H, table, Vs, V, targets, d->ignore_index, yt, s), "target logits");
+  if (st) return st;
+  for (int k = 0; k < d->n_shards; ++k) {
+    const uint16_t* W = static_cast<const uint16_t*>(w_shards[order[k]]);
+    st = hip_status(lce::launch_fwd_round(X, N, H, W, Vs, state, int(p.n_pad), int(p.row_blocks), int(p.splits),
+                                          int(p.tiles_per_split), int(p.col_tiles), k == 0, s),
+                    "forward round");
+    if (st) return st;
+  }
+  return hip_status(lce::launch_finalize(state, int(p.n_pad), int(p.splits), yt, targets, N, d->ignore_index, lse,
+                                         token_loss, part, d->reduction, loss, nvalid, s),
+                    "finalize");
+}
+
+int lce_backward(const lce_dims* d, const void* hidden, const void* const* w_shards, const int32_t* shard_order,
+                 const int32_t* targets, const float* lse, const float* dloss, float* d_hidden,
+                 float* const* d_w_shards, void* workspace, size_t workspace_bytes, void* stream) {
+  Plan p;
+  int st = check_common(d, hidden, w_shards, targets, workspace, workspace_bytes, &p);
+  if (st) return st;
+  if (!lse || !dloss || !d_hidden || !d_w_shards)
+    return fail(LCE_ERR_INVALID_ARG, "lse, dloss, d_hidden and d_w_shards must be non-NULL");
+  if (!aligned16(lse) || !aligned16(d_hidden)) return fail(LCE_ERR_UNSUPPORTED, "lse/d_hidden not 16-byte aligned");
+  for (int k = 0; k < d->n_shards; ++k) {
+    if (!d_w_shards[k]) return fail(LCE_ERR_INVALID_ARG, "d_w_shards[%d] is NULL", k);
+    if (!aligned16(d_w_shards[k])) return fail(LCE_ERR_UNSUPPORTED, "d_w_shards[%d] is not 16-byte aligned", k);
+  }
+  int32_t order[LCE_MAX_SHARDS];
+  st = check_order(shard_order, d->n_shards, order);
+  if (st) return st;
+  g_last_error.clear();
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* gscale = reinterpret_cast<float*>(ws + p.off_gscale);
+  uint16_t* XT = reinterpret_cast<uint16_t*>(ws + p.off_xt);
+  uint16_t* WT = reinterpret_cast<uint16_t*>(ws + p.off_wt);
+  uint16_t* G = reinterpret_cast<uint16_t*>(ws + p.off_g);
+  uint16_t* GT = reinterpret_cast<uint16_t*>(ws + p.off_gt);
+  const uint16_t* X = static_cast<const uint16_t*>(hidden);
+  const int N = int(p.N), H = int(p.H), Vs = int(p.Vs), V = int(p.V), n_pad = int(p.n_pad);
+
+  st = hip_status(lce::launch_bwd_scale(targets, N, d->ignore_index, dloss, d->reduction, gscale, s), "scale");
+  if (st) return st;
+  st = hip_status(lce::launch_transpose(X, N, H, H, XT, n_pad, n_pad, s), "transpose X");
+  if (st) return st;
+  bool first_dx = true;
+  for (int k = 0; k < d->n_shards; ++k) {
+    const int sh = order[k];
+    const uint16_t* W = static_cast<const uint16_t*>(w_shards[sh]);
+    float* dW = d_w_shards[sh];
+    for (int64_t v0 = 0; v0 < p.Vs; v0 += p.vcs) {
+      const int vc = int(std::min<int64_t>(p.vcs, p.Vs - v0));
+      const int vc_pad = int(round_up(vc, kTile));
+      st = hip_status(lce::launch_transpose(W + v0 * p.H, vc, H, H, WT, vc_pad, vc_pad, s), "transpose W");
+      if (st) return st;
+      for (int64_t n0 = 0; n0 < p.N; n0 += p.ncs) {
+        const int nc = int(std::min<int64_t>(p.ncs, p.N - n0));
+        const int nc_pad = int(round_up(nc, kTile));
+        st = hip_status(lce::launch_bwd_g(X, N, H, W, Vs, int(v0), vc, int(n0), nc, targets, lse, gscale,
+                                          d->ignore_index, int(sh * p.Vs + v0), V, G, vc_pad, nc_pad, vc_pad, s),
+                        "gradient block");
+        if (st) return st;
+        st = hip_status(lce::launch_transpose(G, nc_pad, vc_pad, vc_pad, GT, nc_pad, nc_pad, s), "transpose G");
+        if (st) return st;
+        st = hip_status(lce::launch_gemm_acc(G, vc_pad, nc, WT, vc_pad, H, vc_pad, d_hidden + n0 * p.H, H,
+                                             first_dx ? 0 : 1, s),
+                        "dX");
+        if (st) return st;
+        st = hip_status(lce::launch_gemm_acc(GT, nc_pad, vc, XT + n0, n_pad, H, nc_pad, dW + v0 * p.H, H,
+                                             n0 == 0 ? 0 : 1, s),
+                        "dW");
+        if (st) return st;
+      }
+      first_dx = false;
+    }
+  }
+  return LCE_OK;
+}
+
+const char* lce_status_string(int status) {
+  switch (status) {
+    case LCE_OK: return "ok";
+    case LCE_ERR_INVALID_ARG: return "invalid argument";
+    case LCE_ERR_UNSUPPORTED: return "unsupported size or alignment";
+    case LCE_ERR_WORKSPACE: return "workspace too small";
+    case LCE_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* lce_last_error(void) { return g_last_error.c_str(); }
+
+int lce_version(void) { return (1 << 16) | 0; }
+
+}  // extern "C"

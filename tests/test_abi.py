@@ -1,0 +1,140 @@
+"""C-ABI library: loads, exports what include/lce.h declares, and rejects bad
+arguments on the host before any GPU work (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import memory_bounded_vocabulary_amd as lce
+from memory_bounded_vocabulary_amd import Dims
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lce.h")
+FAKE = 0x10000          # a 16-byte-aligned stand-in for a device pointer; never dereferenced
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^LCE_API\s+[\w\s\*]+?\b(lce_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_binding_symbols():
+    assert declared_symbols() == sorted(lce.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = lce.lib()
+    for name in declared_symbols():
+        assert hasattr(L, name), name
+    assert lce.version() == (1, 0)
+
+
+def test_single_hip_runtime_in_process():
+    lce.lib()
+    maps = open("/proc/self/maps").read()
+    paths = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(paths) == 1, paths
+
+
+def _dims(n=256, h=128, v=1024, p=4, ignore=-100, red=0, reserved=0):
+    return Dims(n, h, v, p, ignore, red, reserved)
+
+
+def _fwd(d, hidden=FAKE, shards=None, order=None, targets=FAKE, loss=FAKE, lse=FAKE, tl=None, ws=FAKE,
+         ws_bytes=None):
+    L = lce.lib()
+    p = d.n_shards if d is not None else 1
+    shards = [FAKE] * max(p, 1) if shards is None else shards
+    arr = (ctypes.c_void_p * len(shards))(*shards)
+    if ws_bytes is None:
+        ws_bytes = L.lce_workspace_bytes(ctypes.byref(d)) if d is not None else 0
+    dp = ctypes.byref(d) if d is not None else None
+    ordp = (ctypes.c_int32 * len(order))(*order) if order is not None else None
+    return L.lce_forward(dp, hidden, arr, ordp, targets, loss, lse, tl, ws, ws_bytes, None)
+
+
+def _bwd(d, hidden=FAKE, lse=FAKE, dloss=FAKE, dx=FAKE, dws=None, ws=FAKE, ws_bytes=None, order=None):
+    L = lce.lib()
+    shards = (ctypes.c_void_p * d.n_shards)(*([FAKE] * d.n_shards))
+    dws = [FAKE] * d.n_shards if dws is None else dws
+    dwa = (ctypes.c_void_p * len(dws))(*dws)
+    if ws_bytes is None:
+        ws_bytes = L.lce_workspace_bytes(ctypes.byref(d))
+    ordp = (ctypes.c_int32 * len(order))(*order) if order is not None else None
+    return L.lce_backward(ctypes.byref(d), hidden, shards, ordp, FAKE, lse, dloss, dx, dwa, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("dims,status", [
+    (_dims(n=0), lce.ERR_INVALID_ARG),
+    (_dims(h=0), lce.ERR_INVALID_ARG),
+    (_dims(v=0), lce.ERR_INVALID_ARG),
+    (_dims(p=0), lce.ERR_INVALID_ARG),
+    (_dims(p=257, v=257 * 4), lce.ERR_INVALID_ARG),
+    (_dims(v=1000, p=3), lce.ERR_INVALID_ARG),
+    (_dims(red=2), lce.ERR_INVALID_ARG),
+    (_dims(reserved=1), lce.ERR_INVALID_ARG),
+    (_dims(h=100), lce.ERR_UNSUPPORTED),
+    (_dims(n=1 << 22, h=1024), lce.ERR_UNSUPPORTED),
+])
+def test_bad_dims_rejected(dims, status):
+    L = lce.lib()
+    assert L.lce_workspace_bytes(ctypes.byref(dims)) == 0
+    assert _fwd(dims, ws_bytes=1 << 30) == status
+    assert L.lce_last_error().decode()
+
+
+def test_null_and_misaligned_pointers_rejected():
+    d = _dims()
+    assert _fwd(None) == lce.ERR_INVALID_ARG
+    assert _fwd(d, hidden=None) == lce.ERR_INVALID_ARG
+    assert _fwd(d, targets=None) == lce.ERR_INVALID_ARG
+    assert _fwd(d, loss=None) == lce.ERR_INVALID_ARG
+    assert _fwd(d, lse=None) == lce.ERR_INVALID_ARG
+    assert _fwd(d, ws=None) == lce.ERR_INVALID_ARG
+    assert _fwd(d, shards=[FAKE, FAKE, None, FAKE]) == lce.ERR_INVALID_ARG
+    assert _fwd(d, hidden=FAKE + 8) == lce.ERR_UNSUPPORTED
+    assert _fwd(d, shards=[FAKE, FAKE + 2, FAKE, FAKE]) == lce.ERR_UNSUPPORTED
+    assert _fwd(d, lse=FAKE + 4) == lce.ERR_UNSUPPORTED
+    assert _fwd(d, ws=FAKE + 4) == lce.ERR_UNSUPPORTED
+    assert _bwd(d, dx=None) == lce.ERR_INVALID_ARG
+    assert _bwd(d, dloss=None) == lce.ERR_INVALID_ARG
+    assert _bwd(d, lse=None) == lce.ERR_INVALID_ARG
+    assert _bwd(d, dws=[FAKE, None, FAKE, FAKE]) == lce.ERR_INVALID_ARG
+    assert _bwd(d, dx=FAKE + 4) == lce.ERR_UNSUPPORTED
+
+
+def test_order_must_be_permutation():
+    d = _dims()
+    for bad in ([0, 1, 2, 2], [0, 1, 2, 4], [-1, 0, 1, 2]):
+        assert _fwd(d, order=bad) == lce.ERR_INVALID_ARG
+        assert "permutation" in lce.lib().lce_last_error().decode()
+        assert _bwd(d, order=bad) == lce.ERR_INVALID_ARG
+
+
+def test_workspace_too_small():
+    d = _dims()
+    need = lce.lib().lce_workspace_bytes(ctypes.byref(d))
+    assert need > 0
+    assert _fwd(d, ws_bytes=need - 1) == lce.ERR_WORKSPACE
+    assert _bwd(d, ws_bytes=need - 1) == lce.ERR_WORKSPACE
+    assert "needs %d" % need in lce.lib().lce_last_error().decode()
+
+
+def test_status_strings():
+    L = lce.lib()
+    for st in (0, -1, -2, -3, -4):
+        assert L.lce_status_string(st).decode()
+    assert L.lce_status_string(99).decode() == "unknown status"
+
+
+def test_workspace_is_bounded_independently_of_vocab():
+    # N and H fixed, V swept: the workspace never holds a logit strip (N x V/P)
+    n, h, p = 16384, 4096, 8
+    sizes = [lce.workspace_bytes(n, h, p * vs, p) for vs in (2004, 4008, 8016, 16032, 32064, 64128)]
+    bound = lce.workspace_bytes(n, h, p * 8192, p)   # the largest vocabulary chunk
+    assert max(sizes) <= bound
+    strip_bytes = n * 16032 * 4
+    assert bound < strip_bytes
+    # and it is O(N): doubling V at fixed N never grows it past the bound
+    assert lce.workspace_bytes(n, h, 8 * 128256 * 2, 8) <= bound

@@ -1,0 +1,117 @@
+"""GPU parity on small and degenerate shapes, closed forms and invariants.
+
+Every case runs the HIP path through the C ABI and compares with the CPU
+oracle on the same seeded inputs (gates: |d loss| <= 2e-3, max|d grad| /
+max|grad| <= 2e-2).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_support import GRAD_TOL, compare, oracle_for, rel_max, run_lce, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+BASE = workloads.WORKLOADS["tiny"]
+
+SHAPES = [
+    # name, N, H, V, P, ignore fraction, weight std
+    ("one token", 1, 128, 1024, 4, 0.0, 0.02),
+    ("ragged N=17", 17, 64, 512, 2, 0.2, 0.05),
+    ("N=255 one short of a tile", 255, 192, 768, 3, 0.1, 0.05),
+    ("N=257 one past a tile", 257, 128, 1000, 4, 0.1, 0.05),
+    ("shard of 300 rows (ragged vocab tile)", 600, 256, 1200, 4, 0.05, 0.05),
+    ("single shard", 300, 128, 700, 1, 0.0, 0.05),
+    ("one vocab row per shard", 3, 64, 4, 4, 0.0, 1.0),
+    ("V=1", 5, 64, 1, 1, 0.0, 1.0),
+    ("256 shards", 300, 64, 256 * 3, 256, 0.1, 0.3),
+    ("two token chunks", 16384 + 300, 64, 520, 2, 0.05, 0.3),
+    ("two vocab chunks", 300, 64, 2 * 9000, 2, 0.05, 0.3),
+    ("large logits", 333, 512, 2048, 2, 0.1, 0.5),
+]
+
+
+@pytest.mark.parametrize("case", SHAPES, ids=[s[0] for s in SHAPES])
+def test_shape_parity(case):
+    name, n, h, v, p, ign, std = case
+    say("case", name, dict(N=n, H=h, V=v, P=p))
+    w = BASE.with_dims(name=name, n_tokens=n, hidden=h, vocab=v, n_shards=p, ignore_frac=ign, w_std=std)
+    b = workloads.make(w, seed=3)
+    gpu = run_lce(*to_device(b))
+    compare(gpu, oracle_for(b), name)
+    # ignored tokens: zero loss and exactly zero gradient rows
+    ign_rows = b.targets == -100
+    assert np.all(gpu["token_loss"][ign_rows] == 0.0)
+    assert np.all(gpu["d_hidden"][ign_rows] == 0.0)
+
+
+def test_zero_weight_closed_form():
+    say("case W=0")
+    b = workloads.make("tiny")
+    wz = np.zeros_like(b.weight)
+    gpu = run_lce(*to_device(b, weight=wz))
+    v = BASE.vocab
+    assert abs(gpu["loss"] - math.log(v)) <= 1e-5
+    assert np.all(np.abs(gpu["lse"] - math.log(v)) <= 1e-5)
+    assert np.all(gpu["d_hidden"] == 0.0)
+    x = oracle.bf16_to_f64(b.hidden)
+    g = 1.0 / len(b.targets)
+    expect = np.repeat((g / v) * x.sum(axis=0)[None, :], v, axis=0)
+    np.subtract.at(expect, b.targets, g * x)
+    assert rel_max(gpu["d_weight"], expect) <= GRAD_TOL
+
+
+def test_ring_order_invariance_and_determinism():
+    say("case ring order")
+    w = BASE.with_dims(name="order", n_tokens=700, hidden=256, vocab=8 * 300, n_shards=8, ignore_frac=0.1, w_std=0.2)
+    b = workloads.make(w, seed=5)
+    dev = to_device(b)
+    ref = oracle_for(b)
+    runs = {}
+    for order in ([0, 1, 2, 3, 4, 5, 6, 7], [7, 6, 5, 4, 3, 2, 1, 0], [3, 0, 6, 1, 7, 2, 5, 4], None):
+        r = run_lce(*dev, order=order)
+        compare(r, ref, f"order {order}")
+        runs[str(order)] = r
+    a, c = runs[str([0, 1, 2, 3, 4, 5, 6, 7])], runs[str([7, 6, 5, 4, 3, 2, 1, 0])]
+    assert abs(a["loss"] - c["loss"]) <= 1e-5 * abs(a["loss"])
+    assert rel_max(a["d_hidden"], c["d_hidden"]) <= 2e-3
+    # same order twice: bit-identical (fixed-order reductions, no atomics)
+    again = run_lce(*dev, order=[3, 0, 6, 1, 7, 2, 5, 4])
+    first = runs[str([3, 0, 6, 1, 7, 2, 5, 4])]
+    for k in ("lse", "token_loss", "d_hidden", "d_weight"):
+        assert np.array_equal(again[k], first[k]), k
+    assert again["loss"] == first["loss"]
+
+
+def test_sum_reduction_and_dloss_scale():
+    say("case sum reduction")
+    w = BASE.with_dims(name="sum", n_tokens=300, hidden=128, vocab=1024, n_shards=4, ignore_frac=0.1, w_std=0.1)
+    b = workloads.make(w, seed=7)
+    gpu = run_lce(*to_device(b), reduction="sum", dloss=0.37)
+    ref = oracle_for(b, reduction="sum", dloss=0.37)
+    compare(gpu, ref, "sum", loss_tol=2e-3 * ref.n_valid)
+
+
+def test_all_tokens_ignored():
+    say("case all ignored")
+    w = BASE.with_dims(name="ignored", n_tokens=100, hidden=64, vocab=512, n_shards=2, ignore_frac=1.0)
+    b = workloads.make(w, seed=1)
+    gpu = run_lce(*to_device(b))
+    assert math.isnan(gpu["loss"])
+    assert np.all(gpu["token_loss"] == 0.0)
+    assert np.all(gpu["d_hidden"] == 0.0) and np.all(gpu["d_weight"] == 0.0)
+
+
+def test_out_of_range_target_gives_nan():
+    say("case bad target")
+    w = BASE.with_dims(name="bad", n_tokens=50, hidden=64, vocab=512, n_shards=2, ignore_frac=0.0)
+    b = workloads.make(w, seed=1)
+    b.targets[7] = 512
+    gpu = run_lce(*to_device(b))
+    assert math.isnan(gpu["loss"]) and math.isnan(gpu["token_loss"][7])
+    assert np.all(np.isfinite(np.delete(gpu["token_loss"], 7)))
+    assert np.all(np.isnan(gpu["d_hidden"][7])) and np.all(np.isnan(gpu["d_weight"]))
+    assert np.all(np.isfinite(np.delete(gpu["d_hidden"], 7, axis=0)))
