@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused vocabulary projection + cross-entropy, forward + backward.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload small]
+
+One step = lce_forward + lce_backward over one batch of the workload (all
+shards in ring order), inputs resident in HBM before the timed region. Prints
+one JSON line: tokens/s over the K timed steps, the fraction of MI355X dense
+bf16 MFMA peak the step reaches, peak device bytes, a roofline figure for the
+kernel with the largest share of the step (durations from HIP events recorded
+around every launch on the launching stream), and the CPU oracle timed on a
+bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused linear-CE fwd+bwd tokens/s on 1 MI355X; % bf16 MFMA peak; peak HBM bytes"
+PEAK_BF16_TFLOPS = 2516.6      # dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk/CU
+PEAK_HBM_GBS = 8000.0
+CSRC = os.path.join(ROOT, "memory_bounded_vocabulary_amd", "csrc")
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".hpp", ".cpp")):
+            with open(os.path.join(CSRC, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed PMC summary, if it was taken on this source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rows = json.load(f)
+    sha = kernel_source_sha()
+    for r in rows:
+        if r.get("kernel") == kernel and r.get("workload") == workload and r.get("source_sha") == sha:
+            return r.get("hbm_bytes_per_launch")
+    return None
+
+
+def cpu_baseline(batch, target_s: float):
+    """The oracle as it stands, on the first n' tokens of the same batch (full H, V, P)."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        cores = int(info[0]["num_threads"]) if info else None
+        blas = info[0].get("internal_api") if info else None
+    except Exception:  # pragma: no cover
+        cores, blas = None, None
+    w = batch.workload
+    x_all = batch.hidden
+    wt = oracle.bf16_to_f64(batch.weight)
+
+    def run(n):
+        x = oracle.bf16_to_f64(x_all[:n])
+        t0 = time.perf_counter()
+        oracle.cross_entropy(x, wt, batch.targets[:n])
+        return time.perf_counter() - t0
+
+    n_cal = max(8, min(w.n_tokens, int(2e10 / (6.0 * w.hidden * w.vocab))))
+    t_cal = run(n_cal)
+    n = int(min(w.n_tokens, max(n_cal, n_cal * target_s / max(t_cal, 1e-3))))
+    t = run(n) if n != n_cal else t_cal
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    del np
+    return {"value": n / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {n} of {w.n_tokens} tokens of the {w.name} batch at full H={w.hidden}, "
+                      f"V={w.vocab}, P={w.n_shards}; float64 numpy/BLAS, forward+backward, {t:.1f} s",
+            "blas": blas, "cpu": cpu, "affinity_cores": len(os.sched_getaffinity(0))}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="small")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the ring across P GPUs is a "
+              "design note only). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import memory_bounded_vocabulary_amd as lce
+    import workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    t0 = time.time()
+    batch = workloads.make(w, seed=args.seed)
+    print(f"[bench] {w.name}: N={w.n_tokens} H={w.hidden} V={w.vocab} P={w.n_shards}; "
+          f"inputs drawn in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+    base_alloc = torch.cuda.memory_allocated(dev)
+    hidden = torch.from_numpy(batch.hidden.view(np.int16)).view(torch.bfloat16).to(dev)
+    vs = w.shard_rows
+    shards = [torch.from_numpy(batch.weight[s * vs:(s + 1) * vs].view(np.int16)).view(torch.bfloat16).to(dev)
+              for s in range(w.n_shards)]
+    targets = torch.from_numpy(batch.targets).to(dev)
+    input_bytes = torch.cuda.memory_allocated(dev) - base_alloc
+    d_hidden = torch.empty((w.n_tokens, w.hidden), dtype=torch.float32, device=dev)
+    d_shards = [torch.empty((vs, w.hidden), dtype=torch.float32, device=dev) for _ in range(w.n_shards)]
+    dloss = torch.ones((), dtype=torch.float32, device=dev)
+    ws = lce.alloc_workspace(w.n_tokens, w.hidden, w.vocab, w.n_shards, dev)
+    torch.cuda.synchronize(dev)
+
+    def step():
+        loss, lse = lce.forward(hidden, shards, targets, workspace=ws)
+        lce.backward(hidden, shards, targets, lse, dloss, workspace=ws, d_hidden=d_hidden, d_shards=d_shards)
+        return loss
+
+    for _ in range(args.warmup):
+        loss = step()
+    torch.cuda.synchronize(dev)
+    loss_val = float(loss.item())
+    peak = torch.cuda.max_memory_allocated(dev) - base_alloc
+    output_bytes = (w.n_tokens * w.hidden + w.vocab * w.hidden) * 4 + w.n_tokens * 4 + 4
+
+    # launches per step, to size the event trace
+    lce.trace_enable(1024)
+    step()
+    per_step = sum(e["launches"] for e in lce.trace_collect())
+    lce.trace_enable(per_step * args.steps + 16)
+
+    torch.cuda.synchronize(dev)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        loss = step()
+    end.record()
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - wall0
+    elapsed_ms = start.elapsed_time(end)
+    kernels = lce.trace_collect()
+    lce.trace_enable(0)
+    if not np.isfinite(loss_val):
+        print(f"[bench] loss is not finite: {loss_val}", file=sys.stderr)
+        return 1
+
+    n, h, v = w.n_tokens, w.hidden, w.vocab
+    ms_per_step = elapsed_ms / args.steps
+    tokens_s = n / (ms_per_step / 1e3)
+    flops_8 = 8.0 * n * h * v
+    flops_6 = 6.0 * n * h * v
+    tflops_8 = flops_8 / (ms_per_step / 1e3) / 1e12
+    kern = []
+    for e in kernels:
+        avg_ms = e["total_ms"] / max(e["launches"], 1)
+        kern.append({"kernel": e["name"], "launches_per_step": e["launches"] / args.steps,
+                     "avg_ms": round(avg_ms, 5), "share": round(e["total_ms"] / elapsed_ms, 4),
+                     "tflops": round(e["flops"] / (e["total_ms"] / 1e3) / 1e12, 2) if e["flops"] else None,
+                     "gbs": round(e["bytes"] / (e["total_ms"] / 1e3) / 1e9, 1)})
+    dom = max(kernels, key=lambda e: e["total_ms"])
+    dom_avg_s = dom["total_ms"] / dom["launches"] / 1e3
+    if dom["flops"] > 0:
+        achieved = dom["flops"] / dom["launches"] / dom_avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    else:
+        achieved = dom["bytes"] / dom["launches"] / dom_avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = measured_traffic(dom["name"], w.name)
+    roof["kernel"] = dom["name"]
+    roof["avg_launch_ms"] = round(dom_avg_s * 1e3, 5)
+    roof["algorithmic_per_launch"] = (dom["flops"] if dom["flops"] > 0 else dom["bytes"]) / dom["launches"]
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "n_tokens": n, "hidden": h, "vocab": v, "n_shards": w.n_shards,
+                   "shard_rows": vs, "ignore_frac": w.ignore_frac, "targets": w.targets, "seed": args.seed},
+        "mfma_frac": round(tflops_8 / PEAK_BF16_TFLOPS, 4),
+        "tflops_8nhv": round(tflops_8, 2),
+        "tflops_6nhv": round(flops_6 / (ms_per_step / 1e3) / 1e12, 2),
+        "peak_hbm_bytes": int(peak),
+        "input_bytes": int(input_bytes),
+        "output_bytes": int(output_bytes),
+        "workspace_bytes": int(ws.numel()),
+        "transient_bytes": int(peak - input_bytes - output_bytes),
+        "full_logits_fp32_bytes": int(n) * int(v) * 4,
+        "strip_fp32_bytes": int(n) * int(vs) * 4,
+        "loss": loss_val,
+        "wall_s": round(wall, 3),
+        "roofline": roof,
+        "kernels": kern,
+        "source_sha": kernel_source_sha(),
+        "host": platform.node(),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(batch, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

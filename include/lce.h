@@ -117,6 +117,31 @@ LCE_API int lce_backward(const lce_dims* dims, const void* hidden, const void* c
                  const int32_t* targets, const float* lse, const float* dloss, float* d_hidden,
                  float* const* d_w_shards, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Kernel timing trace, for measurement (off by default).
+ * lce_trace_enable(capacity) creates `capacity` pairs of HIP events for the
+ * calling thread (capacity 0 disables the trace and frees them). While enabled,
+ * every kernel launch made by lce_forward / lce_backward on this thread is
+ * bracketed by an event pair recorded on the call's stream, until the pairs
+ * run out. lce_trace_collect waits for the recorded events, adds the elapsed
+ * times into one entry per kernel kind, writes up to max_entries entries and
+ * returns how many kinds it saw (or a negative status); it then empties the
+ * trace for reuse. Entries also carry the launches' algorithmic work: MFMA
+ * flops (2 x M x N x K of each contraction) and the bytes the kernel must move
+ * at minimum (each operand read once, each output written once).
+ */
+typedef struct lce_trace_entry {
+  char name[32];    /* kernel kind, e.g. "fwd_round", "gemm_dx" */
+  int64_t launches; /* traced launches of this kind */
+  int64_t dropped;  /* launches not traced because the event pairs ran out */
+  double total_ms;  /* sum of event-measured durations of the traced launches */
+  double flops;     /* algorithmic MFMA flops of the traced launches */
+  double bytes;     /* algorithmic bytes of the traced launches */
+} lce_trace_entry;
+
+LCE_API int lce_trace_enable(int capacity);
+LCE_API int lce_trace_collect(lce_trace_entry* out, int max_entries);
+
 /* Static text for a status code. */
 LCE_API const char* lce_status_string(int status);
 

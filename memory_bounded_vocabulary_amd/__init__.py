@@ -23,14 +23,19 @@ LIB_PATH = os.path.join(HERE, "liblce.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 REDUCTIONS = {"mean": 0, "sum": 1}
-EXPORTED = ("lce_workspace_bytes", "lce_forward", "lce_backward", "lce_status_string",
-            "lce_last_error", "lce_version")
+EXPORTED = ("lce_workspace_bytes", "lce_forward", "lce_backward", "lce_trace_enable", "lce_trace_collect",
+            "lce_status_string", "lce_last_error", "lce_version")
 
 
 class Dims(ctypes.Structure):
     _fields_ = [("n_tokens", ctypes.c_int64), ("hidden", ctypes.c_int64), ("vocab", ctypes.c_int64),
                 ("n_shards", ctypes.c_int32), ("ignore_index", ctypes.c_int32),
                 ("reduction", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class TraceEntry(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int64), ("dropped", ctypes.c_int64),
+                ("total_ms", ctypes.c_double), ("flops", ctypes.c_double), ("bytes", ctypes.c_double)]
 
 
 class LceError(RuntimeError):
@@ -60,6 +65,10 @@ def lib() -> ctypes.CDLL:
     L.lce_backward.argtypes = [dimp, vp, ctypes.POINTER(vp), i32p, vp, vp, vp, vp, ctypes.POINTER(vp), vp,
                                ctypes.c_size_t, vp]
     L.lce_backward.restype = ctypes.c_int
+    L.lce_trace_enable.argtypes = [ctypes.c_int]
+    L.lce_trace_enable.restype = ctypes.c_int
+    L.lce_trace_collect.argtypes = [ctypes.POINTER(TraceEntry), ctypes.c_int]
+    L.lce_trace_collect.restype = ctypes.c_int
     L.lce_status_string.argtypes = [ctypes.c_int]
     L.lce_status_string.restype = ctypes.c_char_p
     L.lce_last_error.argtypes = []
@@ -163,6 +172,21 @@ def backward(hidden, shards: Sequence, targets, lse, dloss, ignore_index: int = 
                             workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st)
     return d_hidden, d_shards
+
+
+def trace_enable(capacity: int) -> None:
+    """Bracket each kernel launch of this thread's calls with HIP events (0 disables)."""
+    _check(lib().lce_trace_enable(int(capacity)))
+
+
+def trace_collect() -> List[dict]:
+    """Wait for the traced launches; per kernel kind: launches, ms, algorithmic flops and bytes."""
+    buf = (TraceEntry * 32)()
+    n = lib().lce_trace_collect(buf, 32)
+    if n < 0:
+        _check(n)
+    return [dict(name=e.name.decode(), launches=int(e.launches), dropped=int(e.dropped), total_ms=e.total_ms,
+                 flops=e.flops, bytes=e.bytes) for e in buf[:min(n, 32)]]
 
 
 def version() -> Tuple[int, int]:

@@ -19,6 +19,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "../../include/lce.h"
 #include "lce_internal.hpp"
@@ -170,6 +171,42 @@ int hip_status(hipError_t e, const char* what) {
   return fail(LCE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// ---- optional per-launch event trace (see lce_trace_enable) ----
+enum Kind { kTargetLogit, kFwdRound, kFinalize, kBwdScale, kTransposeX, kTransposeW, kBwdG, kTransposeG,
+            kGemmDx, kGemmDw, kKinds };
+const char* const kKindName[kKinds] = {"target_logit", "fwd_round", "finalize", "bwd_scale", "transpose_x",
+                                       "transpose_w", "bwd_g", "transpose_g", "gemm_dx", "gemm_dw"};
+
+struct Trace {
+  std::vector<hipEvent_t> ev;  // pairs: [2i] before, [2i+1] after launch i
+  struct Rec {
+    int kind;
+    double flops, bytes;
+  };
+  std::vector<Rec> recs;
+  int64_t dropped[kKinds] = {};
+};
+thread_local Trace g_trace;
+
+template <class F>
+hipError_t traced(Kind kind, double flops, double bytes, hipStream_t s, F&& launch) {
+  Trace& t = g_trace;
+  if (t.ev.empty()) return launch();
+  const size_t i = t.recs.size();
+  if (2 * i + 2 > t.ev.size()) {
+    t.dropped[kind]++;
+    return launch();
+  }
+  hipError_t e = hipEventRecord(t.ev[2 * i], s);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(t.ev[2 * i + 1], s);
+  if (e != hipSuccess) return e;
+  t.recs.push_back({int(kind), flops, bytes});
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -204,17 +241,29 @@ int lce_forward(const lce_dims* d, const void* hidden, const void* const* w_shar
 
   lce::ShardTable table{};
   for (int k = 0; k < d->n_shards; ++k) table.p[k] = static_cast<const uint16_t*>(w_shards[k]);
-  st = hip_status(lce::launch_target_logit(X, N, H, table, Vs, V, targets, d->ignore_index, yt, s), "target logits");
+  const double dN = double(p.N), dH = double(p.H), dVs = double(p.Vs), dS = double(p.splits);
+  st = hip_status(traced(kTargetLogit, 0.0, 4.0 * dN * dH + 8.0 * dN, s,
+                         [&] { return lce::launch_target_logit(X, N, H, table, Vs, V, targets, d->ignore_index, yt, s); }),
+                  "target logits");
   if (st) return st;
   for (int k = 0; k < d->n_shards; ++k) {
     const uint16_t* W = static_cast<const uint16_t*>(w_shards[order[k]]);
-    st = hip_status(lce::launch_fwd_round(X, N, H, W, Vs, state, int(p.n_pad), int(p.row_blocks), int(p.splits),
-                                          int(p.tiles_per_split), int(p.col_tiles), k == 0, s),
+    const int first = k == 0;
+    st = hip_status(traced(kFwdRound, 2.0 * dN * dVs * dH, 2.0 * dN * dH + 2.0 * dVs * dH + (first ? 8.0 : 16.0) * dS * dN, s,
+                           [&] {
+                             return lce::launch_fwd_round(X, N, H, W, Vs, state, int(p.n_pad), int(p.row_blocks),
+                                                          int(p.splits), int(p.tiles_per_split), int(p.col_tiles),
+                                                          first, s);
+                           }),
                     "forward round");
     if (st) return st;
   }
-  return hip_status(lce::launch_finalize(state, int(p.n_pad), int(p.splits), yt, targets, N, d->ignore_index, lse,
-                                         token_loss, part, d->reduction, loss, nvalid, s),
+  return hip_status(traced(kFinalize, 0.0, 8.0 * dS * dN + 16.0 * dN, s,
+                           [&] {
+                             return lce::launch_finalize(state, int(p.n_pad), int(p.splits), yt, targets, N,
+                                                         d->ignore_index, lse, token_loss, part, d->reduction, loss,
+                                                         nvalid, s);
+                           }),
                     "finalize");
 }
 
@@ -246,9 +295,14 @@ int lce_backward(const lce_dims* d, const void* hidden, const void* const* w_sha
   const uint16_t* X = static_cast<const uint16_t*>(hidden);
   const int N = int(p.N), H = int(p.H), Vs = int(p.Vs), V = int(p.V), n_pad = int(p.n_pad);
 
-  st = hip_status(lce::launch_bwd_scale(targets, N, d->ignore_index, dloss, d->reduction, gscale, s), "scale");
+  const double dN = double(p.N), dH = double(p.H);
+  st = hip_status(traced(kBwdScale, 0.0, 4.0 * dN, s,
+                         [&] { return lce::launch_bwd_scale(targets, N, d->ignore_index, dloss, d->reduction, gscale, s); }),
+                  "scale");
   if (st) return st;
-  st = hip_status(lce::launch_transpose(X, N, H, H, XT, n_pad, n_pad, s), "transpose X");
+  st = hip_status(traced(kTransposeX, 0.0, 4.0 * dN * dH, s,
+                         [&] { return lce::launch_transpose(X, N, H, H, XT, n_pad, n_pad, s); }),
+                  "transpose X");
   if (st) return st;
   bool first_dx = true;
   for (int k = 0; k < d->n_shards; ++k) {
@@ -258,23 +312,40 @@ int lce_backward(const lce_dims* d, const void* hidden, const void* const* w_sha
     for (int64_t v0 = 0; v0 < p.Vs; v0 += p.vcs) {
       const int vc = int(std::min<int64_t>(p.vcs, p.Vs - v0));
       const int vc_pad = int(round_up(vc, kTile));
-      st = hip_status(lce::launch_transpose(W + v0 * p.H, vc, H, H, WT, vc_pad, vc_pad, s), "transpose W");
+      const double dvc = double(vc);
+      st = hip_status(traced(kTransposeW, 0.0, 4.0 * dvc * dH, s,
+                             [&] { return lce::launch_transpose(W + v0 * p.H, vc, H, H, WT, vc_pad, vc_pad, s); }),
+                      "transpose W");
       if (st) return st;
       for (int64_t n0 = 0; n0 < p.N; n0 += p.ncs) {
         const int nc = int(std::min<int64_t>(p.ncs, p.N - n0));
         const int nc_pad = int(round_up(nc, kTile));
-        st = hip_status(lce::launch_bwd_g(X, N, H, W, Vs, int(v0), vc, int(n0), nc, targets, lse, gscale,
-                                          d->ignore_index, int(sh * p.Vs + v0), V, G, vc_pad, nc_pad, vc_pad, s),
+        const double dnc = double(nc), dgb = 2.0 * double(nc_pad) * double(vc_pad);
+        st = hip_status(traced(kBwdG, 2.0 * dnc * dvc * dH, 2.0 * dnc * dH + 2.0 * dvc * dH + dgb + 12.0 * dnc, s,
+                               [&] {
+                                 return lce::launch_bwd_g(X, N, H, W, Vs, int(v0), vc, int(n0), nc, targets, lse,
+                                                          gscale, d->ignore_index, int(sh * p.Vs + v0), V, G, vc_pad,
+                                                          nc_pad, vc_pad, s);
+                               }),
                         "gradient block");
         if (st) return st;
-        st = hip_status(lce::launch_transpose(G, nc_pad, vc_pad, vc_pad, GT, nc_pad, nc_pad, s), "transpose G");
+        st = hip_status(traced(kTransposeG, 0.0, 2.0 * dgb, s,
+                               [&] { return lce::launch_transpose(G, nc_pad, vc_pad, vc_pad, GT, nc_pad, nc_pad, s); }),
+                        "transpose G");
         if (st) return st;
-        st = hip_status(lce::launch_gemm_acc(G, vc_pad, nc, WT, vc_pad, H, vc_pad, d_hidden + n0 * p.H, H,
-                                             first_dx ? 0 : 1, s),
+        const int acc_dx = first_dx ? 0 : 1, acc_dw = n0 == 0 ? 0 : 1;
+        st = hip_status(traced(kGemmDx, 2.0 * dnc * dH * dvc, 2.0 * dnc * dvc + 2.0 * dH * dvc + (4.0 + 4.0 * acc_dx) * dnc * dH, s,
+                               [&] {
+                                 return lce::launch_gemm_acc(G, vc_pad, nc, WT, vc_pad, H, vc_pad, d_hidden + n0 * p.H,
+                                                             H, acc_dx, s);
+                               }),
                         "dX");
         if (st) return st;
-        st = hip_status(lce::launch_gemm_acc(GT, nc_pad, vc, XT + n0, n_pad, H, nc_pad, dW + v0 * p.H, H,
-                                             n0 == 0 ? 0 : 1, s),
+        st = hip_status(traced(kGemmDw, 2.0 * dvc * dH * dnc, 2.0 * dvc * dnc + 2.0 * dH * dnc + (4.0 + 4.0 * acc_dw) * dvc * dH, s,
+                               [&] {
+                                 return lce::launch_gemm_acc(GT, nc_pad, vc, XT + n0, n_pad, H, nc_pad, dW + v0 * p.H,
+                                                             H, acc_dw, s);
+                               }),
                         "dW");
         if (st) return st;
       }
@@ -282,6 +353,59 @@ int lce_backward(const lce_dims* d, const void* hidden, const void* const* w_sha
     }
   }
   return LCE_OK;
+}
+
+int lce_trace_enable(int capacity) {
+  Trace& t = g_trace;
+  for (hipEvent_t e : t.ev) (void)hipEventDestroy(e);
+  t.ev.clear();
+  t.recs.clear();
+  for (auto& d : t.dropped) d = 0;
+  if (capacity < 0) return fail(LCE_ERR_INVALID_ARG, "trace capacity must be >= 0");
+  t.ev.resize(size_t(2) * capacity);
+  for (auto& e : t.ev) {
+    hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) {
+      t.ev.clear();
+      return hip_status(r, "hipEventCreate");
+    }
+  }
+  t.recs.reserve(capacity);
+  return LCE_OK;
+}
+
+int lce_trace_collect(lce_trace_entry* out, int max_entries) {
+  Trace& t = g_trace;
+  if (max_entries > 0 && !out) return fail(LCE_ERR_INVALID_ARG, "out is NULL");
+  lce_trace_entry agg[kKinds];
+  std::memset(agg, 0, sizeof agg);
+  for (int k = 0; k < kKinds; ++k) {
+    std::snprintf(agg[k].name, sizeof agg[k].name, "%s", kKindName[k]);
+    agg[k].dropped = t.dropped[k];
+  }
+  if (!t.recs.empty()) {
+    int st = hip_status(hipEventSynchronize(t.ev[2 * t.recs.size() - 1]), "hipEventSynchronize");
+    if (st) return st;
+  }
+  for (size_t i = 0; i < t.recs.size(); ++i) {
+    float ms = 0.0f;
+    int st = hip_status(hipEventElapsedTime(&ms, t.ev[2 * i], t.ev[2 * i + 1]), "hipEventElapsedTime");
+    if (st) return st;
+    lce_trace_entry& a = agg[t.recs[i].kind];
+    a.launches += 1;
+    a.total_ms += ms;
+    a.flops += t.recs[i].flops;
+    a.bytes += t.recs[i].bytes;
+  }
+  int n = 0;
+  for (int k = 0; k < kKinds; ++k) {
+    if (agg[k].launches == 0 && agg[k].dropped == 0) continue;
+    if (n < max_entries) out[n] = agg[k];
+    ++n;
+  }
+  t.recs.clear();
+  for (auto& d : t.dropped) d = 0;
+  return n;
 }
 
 const char* lce_status_string(int status) {
