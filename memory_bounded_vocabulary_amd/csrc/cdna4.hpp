@@ -7,6 +7,7 @@
 namespace lce {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -33,6 +34,11 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // lds_wave_base + 16*l. lds_wave_base must be wave-uniform.
 __device__ __forceinline__ void g2lds16(const void* gsrc, LCE_LDS void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(gsrc, lds_wave_base, 16, 0, 0);
+}
+
+// Transposing LDS read (gfx950): see KMajorReader for the lane layout.
+__device__ __forceinline__ bf16x4 ds_read_tr16(const LCE_LDS char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LCE_LDS bf16x4*)p);
 }
 
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

@@ -6,10 +6,11 @@
 //   forward   target logits; round k = 0..P-1 folds shard order[k] into the
 //             per-token running (m, z); finalize lse = m + log z, the token
 //             losses and the loss.
-//   backward  g = dloss / n_valid; X^T once; then for every shard in ring
-//             order and every (vocabulary chunk, token chunk): recompute the
-//             logit block from lse and form G in bf16, then dX += G W_chunk and
-//             dW_chunk += G^T X_chunk (fp32).
+//   backward  g = dloss / n_valid; then for every shard in ring order and
+//             every (vocabulary chunk, token chunk): recompute the logit block
+//             from lse and form G in bf16, then, in one launch, dX += G W_chunk
+//             and dW_chunk += G^T X_chunk (fp32). The GEMMs read W, X and G as
+//             they lie in memory; nothing is transposed.
 // Transient device memory is O(N) plus fixed-size chunks: no logit strip
 // (N x V/P) is ever formed.
 #include <hip/hip_runtime.h>
@@ -52,13 +53,13 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 struct Plan {
   int64_t N, H, V, P, Vs;
-  int64_t n_pad, row_blocks, col_tiles;
+  int64_t n_pad, token_blocks, vocab_tiles;
   int64_t splits, tiles_per_split;
   int64_t vs_pad, vcs, ncs;
   // forward workspace
   size_t off_state, off_yt, off_part, off_nvalid, fwd_bytes;
   // backward workspace
-  size_t off_gscale, off_xt, off_wt, off_g, off_gt, bwd_bytes;
+  size_t off_gscale, off_g, bwd_bytes;
   size_t bytes;
 };
 
@@ -94,12 +95,12 @@ Plan make_plan(const lce_dims* d) {
   p.P = d->n_shards;
   p.Vs = p.V / p.P;
   p.n_pad = round_up(p.N, kTile);
-  p.row_blocks = p.n_pad / kTile;
-  p.col_tiles = ceil_div(p.Vs, kTile);
-  // Split each shard's columns until the grid has about one workgroup per CU.
-  int64_t s = std::min<int64_t>({kMaxSplits, p.col_tiles, std::max<int64_t>(1, ceil_div(kTargetWorkgroups, p.row_blocks))});
-  p.tiles_per_split = ceil_div(p.col_tiles, s);
-  p.splits = ceil_div(p.col_tiles, p.tiles_per_split);
+  p.token_blocks = p.n_pad / kTile;
+  p.vocab_tiles = ceil_div(p.Vs, kTile);
+  // Split each shard's vocabulary tiles until the grid has about one workgroup per CU.
+  int64_t s = std::min<int64_t>({kMaxSplits, p.vocab_tiles, std::max<int64_t>(1, ceil_div(kTargetWorkgroups, p.token_blocks))});
+  p.tiles_per_split = ceil_div(p.vocab_tiles, s);
+  p.splits = ceil_div(p.vocab_tiles, p.tiles_per_split);
   // Backward chunks: balanced, tile-aligned, bounded by constants.
   p.vs_pad = round_up(p.Vs, kTile);
   p.vcs = round_up(ceil_div(p.vs_pad, ceil_div(p.vs_pad, kVocabChunkMax)), kTile);
@@ -111,7 +112,7 @@ Plan make_plan(const lce_dims* d) {
   p.off_yt = o;
   o = align256(o + size_t(p.n_pad) * 4);
   p.off_part = o;
-  o = align256(o + size_t(p.row_blocks) * 16);
+  o = align256(o + size_t(p.token_blocks) * 16);
   p.off_nvalid = o;
   o = align256(o + 16);
   p.fwd_bytes = o;
@@ -119,14 +120,8 @@ Plan make_plan(const lce_dims* d) {
   o = 0;
   p.off_gscale = o;
   o = align256(o + 16);
-  p.off_xt = o;
-  o = align256(o + size_t(p.H) * p.n_pad * 2);
-  p.off_wt = o;
-  o = align256(o + size_t(p.H) * p.vcs * 2);
   p.off_g = o;
   o = align256(o + size_t(p.ncs) * p.vcs * 2);
-  p.off_gt = o;
-  o = align256(o + size_t(p.vcs) * p.ncs * 2);
   p.bwd_bytes = o;
   p.bytes = std::max(p.fwd_bytes, p.bwd_bytes);
   return p;
@@ -172,10 +167,8 @@ int hip_status(hipError_t e, const char* what) {
 }
 
 // ---- optional per-launch event trace (see lce_trace_enable) ----
-enum Kind { kTargetLogit, kFwdRound, kFinalize, kBwdScale, kTransposeX, kTransposeW, kBwdG, kTransposeG,
-            kGemmDx, kGemmDw, kKinds };
-const char* const kKindName[kKinds] = {"target_logit", "fwd_round", "finalize", "bwd_scale", "transpose_x",
-                                       "transpose_w", "bwd_g", "transpose_g", "gemm_dx", "gemm_dw"};
+enum Kind { kTargetLogit, kFwdRound, kFinalize, kBwdScale, kBwdG, kGradGemm, kKinds };
+const char* const kKindName[kKinds] = {"target_logit", "fwd_round", "finalize", "bwd_scale", "bwd_g", "grad_gemm"};
 
 struct Trace {
   std::vector<hipEvent_t> ev;  // pairs: [2i] before, [2i+1] after launch i
@@ -251,8 +244,8 @@ int lce_forward(const lce_dims* d, const void* hidden, const void* const* w_shar
     const int first = k == 0;
     st = hip_status(traced(kFwdRound, 2.0 * dN * dVs * dH, 2.0 * dN * dH + 2.0 * dVs * dH + (first ? 8.0 : 16.0) * dS * dN, s,
                            [&] {
-                             return lce::launch_fwd_round(X, N, H, W, Vs, state, int(p.n_pad), int(p.row_blocks),
-                                                          int(p.splits), int(p.tiles_per_split), int(p.col_tiles),
+                             return lce::launch_fwd_round(X, N, H, W, Vs, state, int(p.n_pad), int(p.token_blocks),
+                                                          int(p.splits), int(p.tiles_per_split), int(p.vocab_tiles),
                                                           first, s);
                            }),
                     "forward round");
@@ -288,23 +281,15 @@ int lce_backward(const lce_dims* d, const void* hidden, const void* const* w_sha
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   float* gscale = reinterpret_cast<float*>(ws + p.off_gscale);
-  uint16_t* XT = reinterpret_cast<uint16_t*>(ws + p.off_xt);
-  uint16_t* WT = reinterpret_cast<uint16_t*>(ws + p.off_wt);
   uint16_t* G = reinterpret_cast<uint16_t*>(ws + p.off_g);
-  uint16_t* GT = reinterpret_cast<uint16_t*>(ws + p.off_gt);
   const uint16_t* X = static_cast<const uint16_t*>(hidden);
-  const int N = int(p.N), H = int(p.H), Vs = int(p.Vs), V = int(p.V), n_pad = int(p.n_pad);
+  const int N = int(p.N), H = int(p.H), Vs = int(p.Vs), V = int(p.V);
 
   const double dN = double(p.N), dH = double(p.H);
   st = hip_status(traced(kBwdScale, 0.0, 4.0 * dN, s,
                          [&] { return lce::launch_bwd_scale(targets, N, d->ignore_index, dloss, d->reduction, gscale, s); }),
                   "scale");
   if (st) return st;
-  st = hip_status(traced(kTransposeX, 0.0, 4.0 * dN * dH, s,
-                         [&] { return lce::launch_transpose(X, N, H, H, XT, n_pad, n_pad, s); }),
-                  "transpose X");
-  if (st) return st;
-  bool first_dx = true;
   for (int k = 0; k < d->n_shards; ++k) {
     const int sh = order[k];
     const uint16_t* W = static_cast<const uint16_t*>(w_shards[sh]);
@@ -313,10 +298,6 @@ int lce_backward(const lce_dims* d, const void* hidden, const void* const* w_sha
       const int vc = int(std::min<int64_t>(p.vcs, p.Vs - v0));
       const int vc_pad = int(round_up(vc, kTile));
       const double dvc = double(vc);
-      st = hip_status(traced(kTransposeW, 0.0, 4.0 * dvc * dH, s,
-                             [&] { return lce::launch_transpose(W + v0 * p.H, vc, H, H, WT, vc_pad, vc_pad, s); }),
-                      "transpose W");
-      if (st) return st;
       for (int64_t n0 = 0; n0 < p.N; n0 += p.ncs) {
         const int nc = int(std::min<int64_t>(p.ncs, p.N - n0));
         const int nc_pad = int(round_up(nc, kTile));
@@ -329,27 +310,18 @@ int lce_backward(const lce_dims* d, const void* hidden, const void* const* w_sha
                                }),
                         "gradient block");
         if (st) return st;
-        st = hip_status(traced(kTransposeG, 0.0, 2.0 * dgb, s,
-                               [&] { return lce::launch_transpose(G, nc_pad, vc_pad, vc_pad, GT, nc_pad, nc_pad, s); }),
-                        "transpose G");
-        if (st) return st;
-        const int acc_dx = first_dx ? 0 : 1, acc_dw = n0 == 0 ? 0 : 1;
-        st = hip_status(traced(kGemmDx, 2.0 * dnc * dH * dvc, 2.0 * dnc * dvc + 2.0 * dH * dvc + (4.0 + 4.0 * acc_dx) * dnc * dH, s,
+        const int acc_dx = (k > 0 || v0 > 0) ? 1 : 0, acc_dw = n0 > 0 ? 1 : 0;
+        const double bytes = 2.0 * dgb + 2.0 * dvc * dH + 2.0 * dnc * dH + (4.0 + 4.0 * acc_dx) * dnc * dH +
+                             (4.0 + 4.0 * acc_dw) * dvc * dH;
+        st = hip_status(traced(kGradGemm, 4.0 * dnc * dvc * dH, bytes, s,
                                [&] {
-                                 return lce::launch_gemm_acc(G, vc_pad, nc, WT, vc_pad, H, vc_pad, d_hidden + n0 * p.H,
-                                                             H, acc_dx, s);
+                                 return lce::launch_grad_gemm(G, vc_pad, nc_pad, vc_pad, W + v0 * p.H, vc,
+                                                              X + n0 * p.H, nc, H, d_hidden + n0 * p.H, acc_dx,
+                                                              dW + v0 * p.H, acc_dw, s);
                                }),
-                        "dX");
-        if (st) return st;
-        st = hip_status(traced(kGemmDw, 2.0 * dvc * dH * dnc, 2.0 * dvc * dnc + 2.0 * dH * dnc + (4.0 + 4.0 * acc_dw) * dvc * dH, s,
-                               [&] {
-                                 return lce::launch_gemm_acc(GT, nc_pad, vc, XT + n0, n_pad, H, nc_pad, dW + v0 * p.H,
-                                                             H, acc_dw, s);
-                               }),
-                        "dW");
+                        "dX and dW");
         if (st) return st;
       }
-      first_dx = false;
     }
   }
   return LCE_OK;

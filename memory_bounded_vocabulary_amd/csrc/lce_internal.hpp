@@ -15,7 +15,7 @@ struct ShardTable {
 };
 
 hipError_t launch_fwd_round(const uint16_t* X, int N, int H, const uint16_t* W, int Vs, float2* state, int state_ld,
-                            int row_blocks, int S, int tiles_per_split, int n_col_tiles, int first, hipStream_t st);
+                            int token_blocks, int S, int tiles_per_split, int n_vtiles, int first, hipStream_t st);
 hipError_t launch_target_logit(const uint16_t* X, int N, int H, const ShardTable& shards, int Vs, int V,
                                const int* targets, int ignore_index, float* yt, hipStream_t st);
 hipError_t launch_finalize(const float2* state, int state_ld, int S, const float* yt, const int* targets, int N,
@@ -26,9 +26,8 @@ hipError_t launch_bwd_scale(const int* targets, int N, int ignore_index, const f
 hipError_t launch_bwd_g(const uint16_t* X, int N, int H, const uint16_t* Ws, int Vs, int v0, int vc, int n0, int nc,
                         const int* targets, const float* lse, const float* gscale, int ignore_index, int vocab_base,
                         int V, uint16_t* G, int ldg, int nc_pad, int vc_pad, hipStream_t st);
-hipError_t launch_transpose(const uint16_t* in, int R, int C, int ld_in, uint16_t* out, int ld_out, int R_pad,
+hipError_t launch_grad_gemm(const uint16_t* G, int ldg, int nc_pad, int vc_pad, const uint16_t* Wc, int vc,
+                            const uint16_t* Xc, int nc, int H, float* dX, int acc_dx, float* dW, int acc_dw,
                             hipStream_t st);
-hipError_t launch_gemm_acc(const uint16_t* A, int lda, int M, const uint16_t* B, int ldb, int Nn, int K, float* C,
-                           int ldc, int accumulate, hipStream_t st);
 
 }  // namespace lce

@@ -17,120 +17,134 @@ namespace lce {
 // --------------------------------------------------------------------------
 // Forward round: fold X W_s^T into the running per-token state.
 //
-// Grid (row_blocks, S). Workgroup (rb, j) owns tokens [256 rb, 256 rb + 256)
-// and the column tiles [j*tps, min((j+1)*tps, n_col_tiles)) of shard s. It
-// keeps, per lane and per token it holds in the MFMA accumulator layout, an
-// online (m, z) in the log2 domain over every column it sees, and merges the
-// lanes and waves once at the end, in a fixed order. The state of split j,
-// state[j][token], is read-modified-written once per round, so over the rounds
-// each split meets the shards in ring order. No atomics: every (j, token) has
-// exactly one writer per launch, and launches are ordered on the stream.
+// The logit tile is computed transposed, W_s rows (vocabulary) x X rows
+// (tokens), so that in the MFMA accumulator layout each lane owns whole token
+// columns: lane l of wave (wm, wn) holds tokens wn*64 + 32 j + l % 32 (j = 0, 1)
+// and, for each, 64 of the tile's 256 vocabulary rows. The online (m, z) of a
+// token therefore lives in two registers per lane and the fold needs no
+// cross-lane traffic until the very end.
+//
+// Grid (token blocks, S splits). Workgroup (tb, s) owns tokens [256 tb, 256 tb
+// + 256) and the vocabulary tiles [s*tps, min((s+1)*tps, n_vtiles)) of the
+// shard. Its (m, z) per token is merged, in a fixed order, into state[s][token]
+// once per round, so over the rounds each split meets the shards in ring
+// order. Every (s, token) has exactly one writer per launch and launches are
+// ordered on the stream: no atomics, bitwise-reproducible.
 // --------------------------------------------------------------------------
-template <int MI, int NI>
-__device__ __forceinline__ void fold_tile(const f32x16 (&acc)[MI][NI], float (&m)[MI * 16], float (&z)[MI * 16],
-                                          const bool (&live)[NI]) {
+__device__ __forceinline__ void fold_full(const Acc& acc, float (&m)[kNI], float (&z)[kNI]) {
 #pragma unroll
-  for (int i = 0; i < MI; ++i) {
-    // One row-block at a time: its NI accumulator vectors leave the AGPRs
-    // together (16 x NI values), are folded row by row, and are released
-    // before the next row-block is touched.
-    f32x16 blk[NI];
+  for (int j = 0; j < kNI; ++j) {
+    float mx = acc[0][j][0];
 #pragma unroll
-    for (int j = 0; j < NI; ++j) blk[j] = acc[i][j];
+    for (int i = 0; i < kMI; ++i)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float v[NI];
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[i][j][e]);
+    const float mn = fmaxf(m[j], mx * kLog2e);
+    float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int j = 0; j < NI; ++j) v[j] = live[j] ? blk[j][e] : -__builtin_inff();
-      float mx = v[0];
+    for (int i = 0; i < kMI; ++i)
 #pragma unroll
-      for (int j = 1; j < NI; ++j) mx = fmaxf(mx, v[j]);
-      const int k = i * 16 + e;
-      const float mn = fmaxf(m[k], mx * kLog2e);
-      float s = 0.0f;
-#pragma unroll
-      for (int j = 0; j < NI; ++j) s += fast_exp2(fmaf(v[j], kLog2e, -mn));
-      z[k] = fmaf(z[k], fast_exp2(m[k] - mn), s);
-      m[k] = mn;
-    }
-    __builtin_amdgcn_sched_barrier(0);
+      for (int e = 0; e < 16; ++e) s[e & 3] += fast_exp2(fmaf(acc[i][j][e], kLog2e, -mn));
+    z[j] = fmaf(z[j], fast_exp2(m[j] - mn), (s[0] + s[1]) + (s[2] + s[3]));
+    m[j] = mn;
   }
 }
 
-template <int WM, int WN>
+// Same, for the shard's last tile: vocabulary rows at or past `live` (relative
+// to this lane's first row) act as -infinity.
+__device__ __forceinline__ void fold_masked(const Acc& acc, float (&m)[kNI], float (&z)[kNI], int live) {
+#pragma unroll
+  for (int j = 0; j < kNI; ++j) {
+    float v[kMI][16];
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int i = 0; i < kMI; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = 32 * i + 8 * (e >> 2) + (e & 3);
+        v[i][e] = r < live ? acc[i][j][e] : -__builtin_inff();
+        mx = fmaxf(mx, v[i][e]);
+      }
+    const float mn = fmaxf(m[j], mx * kLog2e);
+    float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < kMI; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[e & 3] += fast_exp2(fmaf(v[i][e], kLog2e, -mn));
+    z[j] = fmaf(z[j], fast_exp2(m[j] - mn), (s[0] + s[1]) + (s[2] + s[3]));
+    m[j] = mn;
+  }
+}
+
 __global__ __launch_bounds__(kThreads, 1) void fwd_round_kernel(const uint16_t* __restrict__ X, int N, int H,
                                                                 const uint16_t* __restrict__ W, int Vs,
                                                                 float2* __restrict__ state, int state_ld,
-                                                                int tiles_per_split, int n_col_tiles, int first) {
-  using S = TileShape<WM, WN>;
-  constexpr int MI = S::kMI, NI = S::kNI;
-  constexpr int kRedCols = WN * 32;
-  constexpr int kRedStride = kRedCols * 8 + 8;
-  constexpr int kRedBytes = kBM * kRedStride;
-  constexpr int kLdsBytes = kRedBytes > kMainLds ? kRedBytes : kMainLds;
-  __shared__ __attribute__((aligned(1024))) char lds_raw[kLdsBytes];
+                                                                int tiles_per_split, int n_vtiles, int first) {
+  __shared__ __attribute__((aligned(1024))) char lds_raw[kMainLds];
   LCE_LDS char* lds = (LCE_LDS char*)lds_raw;
-  char* ldsg = lds_raw;
-
   const int wave = wave_id();
   const int lane = lane_id();
-  const int row0 = blockIdx.x * kBM;
+  const int wm = wave / kWN, wn = wave % kWN;
+  const int tb = blockIdx.x;
   const int split = blockIdx.y;
   const int t0 = split * tiles_per_split;
-  const int t1 = min(t0 + tiles_per_split, n_col_tiles);
+  const int t1 = min(t0 + tiles_per_split, n_vtiles);
 
-  OperandLoader la;
-  la.init(X, H, row0, N, wave, lane);
-  float m[MI * 16], z[MI * 16];
+  KContigLoader lx;
+  lx.init(X, H, tb * kBN, N, wave, lane);
+  float m[kNI], z[kNI];
 #pragma unroll
-  for (int k = 0; k < MI * 16; ++k) {
-    m[k] = kNegBig;
-    z[k] = 0.0f;
+  for (int j = 0; j < kNI; ++j) {
+    m[j] = kNegBig;
+    z[j] = 0.0f;
   }
-  const int col_lane = (wave % WN) * S::kWaveN + (lane & 31);
-  for (int ct = t0; ct < t1; ++ct) {
-    OperandLoader lb;
-    lb.init(W, H, ct * kBN, Vs, wave, lane);
-    f32x16 acc[MI][NI];
-    tile_mainloop<WM, WN>(la, lb, H, lds, acc, false);
-    // columns past the end of the shard (last tile only) act as -infinity
-    const int cvalid = Vs - ct * kBN;
-    bool live[NI];
-#pragma unroll
-    for (int j = 0; j < NI; ++j) live[j] = col_lane + j * 32 < cvalid;
-    fold_tile<MI, NI>(acc, m, z, live);
+  const int lane_row = wm * kWaveM + 4 * (lane >> 5);  // first vocabulary row of this lane in a tile
+  for (int vt = t0; vt < t1; ++vt) {
+    KContigLoader lw;
+    lw.init(W, H, vt * kBM, Vs, wave, lane);
+    Acc acc;
+    tile_mainloop<false, false>(lw, lx, H, lds, acc);
+    const int live = Vs - vt * kBM;
+    if (live >= kBM)
+      fold_full(acc, m, z);
+    else
+      fold_masked(acc, m, z, live - lane_row);
   }
 
-  // Merge lanes and waves: every lane parks its (m, z) per token in LDS, then
-  // thread t merges token t's partials in column order.
-  const int rcol = (wave % WN) * 32 + (lane & 31);
+  // lanes l and l ^ 32 hold the same tokens (different vocabulary rows)
 #pragma unroll
-  for (int i = 0; i < MI; ++i)
+  for (int j = 0; j < kNI; ++j) {
+    const float m2 = __shfl_xor(m[j], 32);
+    const float z2 = __shfl_xor(z[j], 32);
+    lse_merge(m[j], z[j], m2, z2);
+  }
+  // waves wm = 1 hand their tokens' state to waves wm = 0 (LDS is free: the
+  // main loop ended on a barrier)
+  float2* red = reinterpret_cast<float2*>(lds_raw);
+  if (wm == 1 && lane < 32) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int r = acc_row<WM, WN>(wave, lane, i, e);
-      float* d = reinterpret_cast<float*>(ldsg + r * kRedStride + rcol * 8);
-      d[0] = m[i * 16 + e];
-      d[1] = z[i * 16 + e];
-    }
+    for (int j = 0; j < kNI; ++j) red[wn * kWaveN + 32 * j + lane] = make_float2(m[j], z[j]);
+  }
   __syncthreads();
-  const int r = threadIdx.x;
-  float M = kNegBig, Z = 0.0f;
-  for (int c = 0; c < kRedCols; ++c) {
-    const float* p = reinterpret_cast<const float*>(ldsg + r * kRedStride + c * 8);
-    lse_merge(M, Z, p[0], p[1]);
-  }
-  const int row = row0 + r;
-  if (row < N) {
-    float2* sp = state + (size_t)split * state_ld + row;
-    if (!first) {
-      const float2 o = *sp;
-      float M0 = o.x, Z0 = o.y;
-      lse_merge(M0, Z0, M, Z);
-      M = M0;
-      Z = Z0;
+  if (wm == 0 && lane < 32) {
+#pragma unroll
+    for (int j = 0; j < kNI; ++j) {
+      const float2 o = red[wn * kWaveN + 32 * j + lane];
+      float M = m[j], Z = z[j];
+      lse_merge(M, Z, o.x, o.y);
+      const int row = tb * kBN + wn * kWaveN + 32 * j + lane;
+      if (row < N) {
+        float2* sp = state + (size_t)split * state_ld + row;
+        if (!first) {
+          const float2 p = *sp;
+          float M0 = p.x, Z0 = p.y;
+          lse_merge(M0, Z0, M, Z);
+          M = M0;
+          Z = Z0;
+        }
+        *sp = make_float2(M, Z);
+      }
     }
-    *sp = make_float2(M, Z);
   }
 }
 
@@ -250,20 +264,16 @@ __global__ __launch_bounds__(256) void bwd_scale_kernel(const int* __restrict__ 
 }
 
 // --------------------------------------------------------------------------
-// Backward recompute of one 256x256 logit tile of the (token chunk, vocabulary
-// chunk) block and its gradient G = g_i (exp(y - lse_i) - [v == t_i]) in bf16
-// (round to nearest even). Rows past the token chunk and columns past the
-// vocabulary chunk are written as 0, so G is a dense zero-padded
-// [nc_pad][vc_pad] matrix.
+// Backward recompute of one 256 x 256 block of the (token chunk, vocabulary
+// chunk) logits and its gradient G = g_i (exp(y - lse_i) - [v == t_i]) in bf16
+// (round to nearest even), written to G [token][vocabulary] (row pitch ldg).
+// As in the forward, the tile is computed vocabulary x token, so each lane
+// owns two token columns and their (lse, g, target) sit in registers. Rows
+// past the token chunk (g = 0, lse = +inf) and columns past the vocabulary
+// chunk are written as 0, so G is a dense zero-padded [nc_pad][vc_pad] matrix.
+// The tile is staged in LDS (16-byte chunks of each token row XOR-swizzled by
+// the row) and written out with 16-byte stores.
 // --------------------------------------------------------------------------
-struct RowInfo {
-  float lse2;
-  float g;
-  int tcol;
-  int pad;
-};
-
-template <int WM, int WN>
 __global__ __launch_bounds__(kThreads, 1) void bwd_g_kernel(const uint16_t* __restrict__ X, int N, int H,
                                                             const uint16_t* __restrict__ Ws, int Vs, int v0,
                                                             int vc, int n0, int nc,
@@ -272,133 +282,95 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_g_kernel(const uint16_t* __re
                                                             const float* __restrict__ gscale, int ignore_index,
                                                             int vocab_base, int V, uint16_t* __restrict__ G,
                                                             int ldg) {
-  using S = TileShape<WM, WN>;
-  constexpr int MI = S::kMI, NI = S::kNI;
-  constexpr int kStgStride = (kBN + 8) * 2;  // bytes per staged bf16 row
-  constexpr int kStgBytes = kBM * kStgStride;
-  constexpr int kBodyBytes = kStgBytes > kMainLds ? kStgBytes : kMainLds;
-  __shared__ __attribute__((aligned(1024))) char lds_raw[kBodyBytes + kBM * (int)sizeof(RowInfo)];
-  LCE_LDS char* lds = (LCE_LDS char*)lds_raw;
-  char* ldsg = lds_raw;
-  RowInfo* info = reinterpret_cast<RowInfo*>(ldsg + kBodyBytes);
-
-  const int wave = wave_id();
-  const int lane = lane_id();
-  const int tm = blockIdx.x, tn = blockIdx.y;
-  {
-    const int rr = tm * kBM + threadIdx.x;
-    const int row = n0 + rr;
-    RowInfo ri{__builtin_inff(), 0.0f, -1, 0};
-    if (rr < nc && row < N) {
-      ri.lse2 = lse[row] * kLog2e;
-      const int t = targets[row];
-      if (t != ignore_index) {
-        if (t < 0 || t >= V) {
-          ri.g = __builtin_nanf("");
-        } else {
-          ri.g = gscale[0];
-          ri.tcol = t - (vocab_base + tn * kBN);
-        }
-      }
-    }
-    info[threadIdx.x] = ri;
-  }
-  OperandLoader la, lb;
-  la.init(X, H, n0 + tm * kBM, N, wave, lane);
-  lb.init(Ws, H, v0 + tn * kBN, Vs, wave, lane);
-  f32x16 acc[MI][NI];
-  tile_mainloop<WM, WN>(la, lb, H, lds, acc, false);  // its barriers also publish info[]
-
-  const int cvalid = vc - tn * kBN;
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int r = acc_row<WM, WN>(wave, lane, i, e);
-      const RowInfo ri = info[r];
-#pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        const int c = acc_col<WM, WN>(wave, lane, j);
-        const float p = fast_exp2(fmaf(acc[i][j][e], kLog2e, -ri.lse2));
-        float gv = ri.g * (p - (c == ri.tcol ? 1.0f : 0.0f));
-        if (c >= cvalid) gv = 0.0f;
-        *reinterpret_cast<uint16_t*>(ldsg + r * kStgStride + c * 2) = f32_to_bf16(gv);
-      }
-    }
-  __syncthreads();
-  uint16_t* gt = G + (size_t)tm * kBM * ldg + (size_t)tn * kBN;
-#pragma unroll 4
-  for (int it = 0; it < kBM * kBN / 8 / kThreads; ++it) {
-    const int q = it * kThreads + threadIdx.x;
-    const int r = q >> 5, c8 = q & 31;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(ldsg + r * kStgStride + c8 * 16);
-    *reinterpret_cast<u32x4*>(gt + (size_t)r * ldg + c8 * 8) = v;
-  }
-}
-
-// --------------------------------------------------------------------------
-// out[c][r] = in[r][c] for r < R, c < C; out[c][r] = 0 for R <= r < R_pad.
-// 64x64 tiles through LDS. C, ld_in, ld_out and R_pad are multiples of 8.
-// --------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ in, int R, int C,
-                                                             int ld_in, uint16_t* __restrict__ out, int ld_out,
-                                                             int R_pad) {
-  __shared__ uint16_t t[64][72];
-  const int br = blockIdx.x * 64, bc = blockIdx.y * 64;
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int q = threadIdx.x + 256 * k;
-    const int r = q >> 3, c8 = (q & 7) * 8;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (br + r < R && bc + c8 < C) v = *reinterpret_cast<const u32x4*>(in + (size_t)(br + r) * ld_in + bc + c8);
-    *reinterpret_cast<u32x4*>(&t[r][c8]) = v;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int q = threadIdx.x + 256 * k;
-    const int c = q >> 3, r8 = (q & 7) * 8;
-    if (bc + c < C && br + r8 < R_pad) {
-      u32x4 v;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) v[p] = (uint32_t)t[r8 + 2 * p][c] | ((uint32_t)t[r8 + 2 * p + 1][c] << 16);
-      *reinterpret_cast<u32x4*>(out + (size_t)(bc + c) * ld_out + br + r8) = v;
-    }
-  }
-}
-
-// --------------------------------------------------------------------------
-// C[M][Nn] (+)= A[M][K] B[Nn][K]^T in fp32, one 256x256 tile per workgroup.
-// K is a multiple of 64. Rows of A past M and of B past Nn load clamped rows;
-// their results are not stored.
-// --------------------------------------------------------------------------
-template <int WM, int WN>
-__global__ __launch_bounds__(kThreads, 1) void gemm_acc_kernel(const uint16_t* __restrict__ A, int lda, int M,
-                                                               const uint16_t* __restrict__ B, int ldb, int Nn,
-                                                               int K, float* __restrict__ C, int ldc,
-                                                               int accumulate) {
-  using S = TileShape<WM, WN>;
-  constexpr int MI = S::kMI, NI = S::kNI;
   __shared__ __attribute__((aligned(1024))) char lds_raw[kMainLds];
   LCE_LDS char* lds = (LCE_LDS char*)lds_raw;
   const int wave = wave_id();
   const int lane = lane_id();
-  const int tm = blockIdx.x, tn = blockIdx.y;
-  OperandLoader la, lb;
-  la.init(A, lda, tm * kBM, M, wave, lane);
-  lb.init(B, ldb, tn * kBN, Nn, wave, lane);
-  f32x16 acc[MI][NI];
-  tile_mainloop<WM, WN>(la, lb, K, lds, acc, false);
+  const int wm = wave / kWN, wn = wave % kWN;
+  const int tv = blockIdx.x, tt = blockIdx.y;
+
+  // per-lane token info: log2-domain lse, gradient scale, target row in this tile
+  float lse2[kNI], g[kNI];
+  int tcol[kNI];
 #pragma unroll
-  for (int i = 0; i < MI; ++i)
+  for (int j = 0; j < kNI; ++j) {
+    const int rr = tt * kBN + wn * kWaveN + 32 * j + (lane & 31);
+    const int row = n0 + rr;
+    lse2[j] = __builtin_inff();
+    g[j] = 0.0f;
+    tcol[j] = -1;
+    if (rr < nc && row < N) {
+      lse2[j] = lse[row] * kLog2e;
+      const int t = targets[row];
+      if (t != ignore_index) {
+        if (t < 0 || t >= V) {
+          g[j] = __builtin_nanf("");
+        } else {
+          g[j] = gscale[0];
+          tcol[j] = t - (vocab_base + tv * kBM);
+        }
+      }
+    }
+  }
+  KContigLoader lw, lx;
+  lw.init(Ws, H, v0 + tv * kBM, Vs, wave, lane);
+  lx.init(X, H, n0 + tt * kBN, N, wave, lane);
+  Acc acc;
+  tile_mainloop<false, false>(lw, lx, H, lds, acc);
+
+  const int live = vc - tv * kBM;  // vocabulary rows of this tile inside the chunk
+#pragma unroll
+  for (int j = 0; j < kNI; ++j) {
+    const int tok = wn * kWaveN + 32 * j + (lane & 31);  // token row of the staged tile
+#pragma unroll
+    for (int i = 0; i < kMI; ++i)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int r0 = wm * kWaveM + 32 * i + 8 * e4 + 4 * (lane >> 5);  // 4 consecutive vocabulary rows
+        float gv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = r0 + q;
+          const float p = fast_exp2(fmaf(acc[i][j][4 * e4 + q], kLog2e, -lse2[j]));
+          const float v = g[j] * (p - (r == tcol[j] ? 1.0f : 0.0f));
+          gv[q] = r < live ? v : 0.0f;
+        }
+        const int slot = (r0 >> 3) ^ (tok & 31);
+        uint2 packed = make_uint2(pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3]));
+        *reinterpret_cast<uint2*>(lds_raw + tok * 512 + slot * 16 + (r0 & 7) * 2) = packed;
+      }
+  }
+  __syncthreads();
+  uint16_t* gt = G + (size_t)tt * kBN * ldg + (size_t)tv * kBM;
+#pragma unroll 4
+  for (int it = 0; it < kBN * kBM / 8 / kThreads; ++it) {
+    const int q = it * kThreads + threadIdx.x;
+    const int r = q >> 5, c = q & 31;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(lds_raw + r * 512 + ((c ^ (r & 31)) << 4));
+    *reinterpret_cast<u32x4*>(gt + (size_t)r * ldg + c * 8) = v;
+  }
+}
+
+// --------------------------------------------------------------------------
+// Both gradient contractions of one (token chunk, vocabulary chunk) block in
+// one launch, each 256 x 256 output tile a workgroup:
+//   tiles [0, dx_tiles):   dX[n0 + m][h]  (+)= sum_v G[m][v] W_s[v0 + v][h]
+//   tiles [dx_tiles, ..):  dW_s[v0 + m][h] (+)= sum_t G[t][m] X[n0 + t][h]
+// G is read as it was written: K-contiguous for dX, K-major for dW; W_s and X
+// are K-major for both. Output tiles are stored (or added) in fp32.
+// --------------------------------------------------------------------------
+__device__ __forceinline__ void store_tile(const Acc& acc, float* __restrict__ C, int ldc, int m0, int m_valid,
+                                           int n0, int n_valid, int accumulate, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < kMI; ++i)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int r = tm * kBM + acc_row<WM, WN>(wave, lane, i, e);
-      if (r >= M) continue;
+      const int r = m0 + acc_row(wave, lane, i, e);
+      if (r >= m_valid) continue;
 #pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        const int c = tn * kBN + acc_col<WM, WN>(wave, lane, j);
-        if (c < Nn) {
+      for (int j = 0; j < kNI; ++j) {
+        const int c = n0 + acc_col(wave, lane, j);
+        if (c < n_valid) {
           float* p = C + (size_t)r * ldc + c;
           *p = accumulate ? *p + acc[i][j][e] : acc[i][j][e];
         }
@@ -406,19 +378,44 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_acc_kernel(const uint16_t* _
     }
 }
 
-// ============================ host launchers ==============================
-// Wave layouts (WM x WN): the forward keeps a per-lane online state for every
-// token it holds, so it uses 4x1 (64 tokens x 256 columns per wave, 32 tokens
-// per lane); the others use 2x2 (128 x 128 per wave).
-constexpr int kFwdWM = 4, kFwdWN = 1;
-constexpr int kWM = 2, kWN = 2;
+__global__ __launch_bounds__(kThreads, 1) void grad_gemm_kernel(const uint16_t* __restrict__ G, int ldg, int nc_pad,
+                                                                int vc_pad, const uint16_t* __restrict__ Wc, int vc,
+                                                                const uint16_t* __restrict__ Xc, int nc, int H,
+                                                                float* __restrict__ dX, int acc_dx,
+                                                                float* __restrict__ dW, int acc_dw, int dx_tiles,
+                                                                int n_tiles) {
+  __shared__ __attribute__((aligned(1024))) char lds_raw[kMainLds];
+  LCE_LDS char* lds = (LCE_LDS char*)lds_raw;
+  const int wave = wave_id();
+  const int lane = lane_id();
+  int id = blockIdx.x;
+  Acc acc;
+  if (id < dx_tiles) {
+    const int tm = id / n_tiles, tn = id % n_tiles;
+    KContigLoader la;
+    KMajorLoader lb;
+    la.init(G, ldg, tm * kBM, nc_pad, wave, lane);
+    lb.init(Wc, H, tn * kBN, H, vc, wave, lane);
+    tile_mainloop<false, true>(la, lb, vc_pad, lds, acc);
+    store_tile(acc, dX, H, tm * kBM, nc, tn * kBN, H, acc_dx, wave, lane);
+  } else {
+    id -= dx_tiles;
+    const int tm = id / n_tiles, tn = id % n_tiles;
+    KMajorLoader la, lb;
+    la.init(G, ldg, tm * kBM, vc_pad, nc_pad, wave, lane);
+    lb.init(Xc, H, tn * kBN, H, nc, wave, lane);
+    tile_mainloop<true, true>(la, lb, nc_pad, lds, acc);
+    store_tile(acc, dW, H, tm * kBM, vc, tn * kBN, H, acc_dw, wave, lane);
+  }
+}
 
+// ============================ host launchers ==============================
 static inline hipError_t last() { return hipGetLastError(); }
 
 hipError_t launch_fwd_round(const uint16_t* X, int N, int H, const uint16_t* W, int Vs, float2* state, int state_ld,
-                            int row_blocks, int S, int tiles_per_split, int n_col_tiles, int first, hipStream_t st) {
-  hipLaunchKernelGGL((fwd_round_kernel<kFwdWM, kFwdWN>), dim3(row_blocks, S), dim3(kThreads), 0, st, X, N, H, W, Vs,
-                     state, state_ld, tiles_per_split, n_col_tiles, first);
+                            int token_blocks, int S, int tiles_per_split, int n_vtiles, int first, hipStream_t st) {
+  hipLaunchKernelGGL(fwd_round_kernel, dim3(token_blocks, S), dim3(kThreads), 0, st, X, N, H, W, Vs, state, state_ld,
+                     tiles_per_split, n_vtiles, first);
   return last();
 }
 
@@ -450,22 +447,19 @@ hipError_t launch_bwd_scale(const int* targets, int N, int ignore_index, const f
 hipError_t launch_bwd_g(const uint16_t* X, int N, int H, const uint16_t* Ws, int Vs, int v0, int vc, int n0, int nc,
                         const int* targets, const float* lse, const float* gscale, int ignore_index, int vocab_base,
                         int V, uint16_t* G, int ldg, int nc_pad, int vc_pad, hipStream_t st) {
-  hipLaunchKernelGGL((bwd_g_kernel<kWM, kWN>), dim3(nc_pad / kBM, vc_pad / kBN), dim3(kThreads), 0, st, X, N, H, Ws,
-                     Vs, v0, vc, n0, nc, targets, lse, gscale, ignore_index, vocab_base, V, G, ldg);
+  hipLaunchKernelGGL(bwd_g_kernel, dim3(vc_pad / kBM, nc_pad / kBN), dim3(kThreads), 0, st, X, N, H, Ws, Vs, v0, vc,
+                     n0, nc, targets, lse, gscale, ignore_index, vocab_base, V, G, ldg);
   return last();
 }
 
-hipError_t launch_transpose(const uint16_t* in, int R, int C, int ld_in, uint16_t* out, int ld_out, int R_pad,
+hipError_t launch_grad_gemm(const uint16_t* G, int ldg, int nc_pad, int vc_pad, const uint16_t* Wc, int vc,
+                            const uint16_t* Xc, int nc, int H, float* dX, int acc_dx, float* dW, int acc_dw,
                             hipStream_t st) {
-  hipLaunchKernelGGL(transpose_bf16_kernel, dim3((R_pad + 63) / 64, (C + 63) / 64), dim3(256), 0, st, in, R, C, ld_in,
-                     out, ld_out, R_pad);
-  return last();
-}
-
-hipError_t launch_gemm_acc(const uint16_t* A, int lda, int M, const uint16_t* B, int ldb, int Nn, int K, float* C,
-                           int ldc, int accumulate, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_acc_kernel<kWM, kWN>), dim3((M + kBM - 1) / kBM, (Nn + kBN - 1) / kBN), dim3(kThreads), 0,
-                     st, A, lda, M, B, ldb, Nn, K, C, ldc, accumulate);
+  const int n_tiles = H / kBN + (H % kBN ? 1 : 0);
+  const int dx_tiles = (nc_pad / kBM) * n_tiles;
+  const int dw_tiles = (vc_pad / kBM) * n_tiles;
+  hipLaunchKernelGGL(grad_gemm_kernel, dim3(dx_tiles + dw_tiles), dim3(kThreads), 0, st, G, ldg, nc_pad, vc_pad, Wc,
+                     vc, Xc, nc, H, dX, acc_dx, dW, acc_dw, dx_tiles, n_tiles);
   return last();
 }
 

@@ -1,20 +1,32 @@
-// One 256x256 output tile of C = A * B^T on CDNA4 bf16 MFMA, with A [M][K] and
-// B [N][K] both K-contiguous ("NT"). Every contraction of the path has this
-// shape: the forward logit tile X W_s^T and its backward recompute (K = H),
-// dX = G (W_s^T)^T (K = vocabulary chunk) and dW_s = G^T (X^T)^T (K = token
-// chunk), the last two fed with transposed copies so both operands stay
-// K-contiguous.
+// One 256x256 output tile of C[m][n] = sum_k A(m, k) B(n, k) on CDNA4 bf16 MFMA.
 //
-// Workgroup: 256 threads = 4 waves of 64, arranged WM x WN over the tile; each
-// wave owns a (256/WM) x (256/WN) sub-tile held as 32x32 MFMA accumulators.
-// K advances 64 at a time through two LDS stages of 64 KB (A and B, 32 KB
-// each), filled by direct global->LDS 16-byte loads (no VGPR staging) while
-// the MFMAs run on the other stage.
+// Every contraction of the path is one of these, with each operand stored in
+// global memory either K-contiguous ("row" m holds its K values contiguously)
+// or K-major (row k holds 256+ consecutive m values contiguously):
+//   logit tile (forward and backward recompute)  A = W_s rows, B = X rows, K = H,
+//                                                both K-contiguous;
+//   dX += G W_s       A = G [token][vocab] (K-contiguous), B = W_s [vocab][H] (K-major);
+//   dW_s += G^T X     A = G [token][vocab] (K-major), B = X [token][H] (K-major).
+// No operand is ever transposed in memory: K-major tiles are copied to LDS as
+// they are, and the fragment reads transpose them (ds_read_tr16_b64).
 //
-// LDS layout of one operand stage: 256 rows x 128 bytes (64 bf16 of K), as
-// 16-byte chunks. Chunk kc of row r sits in slot kc ^ (r & 7) ^ ((r >> 3) & 1),
-// so the 16-byte fragment reads of 8 consecutive rows (32-bank phases) and of
-// 16 consecutive rows (64-bank phases) each touch distinct banks.
+// Workgroup: 512 threads = 8 waves, two per SIMD, arranged 2 (M) x 4 (N); each
+// wave owns a 128 x 64 sub-tile held as 4 x 2 accumulators of the 32x32x16 bf16
+// MFMA (128 fp32 per lane). Two waves per SIMD let one wave's LDS traffic and
+// waits hide under the other's MFMAs.
+//
+// K advances 64 per stage through two LDS stages (A and B, 32 KB each, 128 KB
+// total) filled by direct global->LDS 16-byte loads. Within a stage, the
+// fragments of k-step s+1 are read from LDS while the MFMAs of k-step s run;
+// the loads of the next stage are in flight during the whole stage.
+//
+// LDS layouts (one operand, one stage, 32 KB):
+//  K-contiguous: 256 rows x 128 bytes (64 bf16 of K), as 16-byte chunks; chunk
+//    kc of row r sits in slot kc ^ swz(r), so the 16-byte fragment reads of 8
+//    (and 16) consecutive rows fall in distinct banks.
+//  K-major: 64 rows (k) x 512 bytes (256 bf16 of m); 16-byte chunk c of row k
+//    sits in slot c ^ kmaj_swz(k), so the four 32-byte row segments one 16-lane
+//    group of a transposing read touches (rows k..k+3) fall in distinct banks.
 #pragma once
 #include "cdna4.hpp"
 
@@ -23,123 +35,227 @@ namespace lce {
 constexpr int kBM = 256;
 constexpr int kBN = 256;
 constexpr int kBK = 64;
-constexpr int kThreads = 256;
-constexpr int kTileBytes = kBM * kBK * 2;      // one operand, one stage: 32 KB
-constexpr int kStageBytes = 2 * kTileBytes;    // A + B
-constexpr int kMainLds = 2 * kStageBytes;      // double-buffered: 128 KB
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kOpBytes = kBM * kBK * 2;      // one operand, one stage: 32 KB
+constexpr int kStageBytes = 2 * kOpBytes;    // A + B
+constexpr int kMainLds = 2 * kStageBytes;    // double-buffered: 128 KB
+
+constexpr int kWM = 2, kWN = 4;              // wave grid over the tile
+constexpr int kWaveM = kBM / kWM;            // 128
+constexpr int kWaveN = kBN / kWN;            // 64
+constexpr int kMI = kWaveM / 32;             // 4 accumulator rows of blocks
+constexpr int kNI = kWaveN / 32;             // 2 accumulator columns of blocks
+
+typedef f32x16 Acc[kMI][kNI];
 
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int kmaj_swz(int k) { return (2 * (k & 3)) ^ (8 * (k & 1)); }
 
-// Global -> LDS loader for one 256-row operand. Rows at or past rows_valid are
-// clamped to the last valid row: they load real (finite) data whose results the
-// epilogues discard.
-struct OperandLoader {
+// ---- global -> LDS loaders ------------------------------------------------
+// Each wave issues 4 loads of 1 KB (64 lanes x 16 bytes) per operand and stage.
+
+// K-contiguous operand: tile rows row0..row0+255 of a [rows][ld] bf16 matrix.
+// Rows at or past rows_valid are clamped to the last valid row: they load real
+// (finite) data whose results the epilogues discard or whose partner operand
+// is zero there.
+struct KContigLoader {
   const char* base;
-  uint32_t off[8];
+  uint32_t off[4];
 
   __device__ __forceinline__ void init(const uint16_t* p, int ld, int row0, int rows_valid, int wave, int lane) {
     base = reinterpret_cast<const char*>(p);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      int r = wave * 64 + j * 8 + (lane >> 3);
-      int kc = (lane & 7) ^ (((lane >> 3) & 7) ^ (j & 1));
-      int gr = min(row0 + r, rows_valid - 1);
+    for (int j = 0; j < 4; ++j) {
+      const int r = wave * 32 + j * 8 + (lane >> 3);
+      const int kc = (lane & 7) ^ swz(r);
+      const int gr = min(row0 + r, rows_valid - 1);
       off[j] = (uint32_t)gr * (uint32_t)ld * 2u + (uint32_t)kc * 16u;
     }
   }
   __device__ __forceinline__ void issue(int k0, LCE_LDS char* tile, int wave) const {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      g2lds16(base + off[j] + (uint32_t)k0 * 2u, tile + (wave * 8 + j) * 1024);
+    for (int j = 0; j < 4; ++j) g2lds16(base + off[j] + (uint32_t)k0 * 2u, tile + (wave * 4 + j) * 1024);
   }
 };
 
-template <int WM, int WN>
-struct TileShape {
-  static constexpr int kWaveM = kBM / WM;
-  static constexpr int kWaveN = kBN / WN;
-  static constexpr int kMI = kWaveM / 32;
-  static constexpr int kNI = kWaveN / 32;
-  static_assert(WM * WN == 4, "four waves per workgroup");
+// K-major operand: element (m, k) at p[k * ld + m]; the tile covers columns
+// m0..m0+255 and rows k0..k0+63. Columns past m_valid (a multiple of 8) and
+// rows past k_valid are clamped to the last valid ones.
+struct KMajorLoader {
+  const char* base;
+  uint32_t ld2;       // row pitch in bytes
+  uint32_t col[4];    // byte offset of this lane's 16-byte chunk within a row
+  int row[4];         // tile row (k) this lane fills, per load
+  int k_last;
+
+  __device__ __forceinline__ void init(const uint16_t* p, int ld, int m0, int m_valid, int k_valid, int wave,
+                                       int lane) {
+    base = reinterpret_cast<const char*>(p);
+    ld2 = (uint32_t)ld * 2u;
+    k_last = k_valid - 1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q = wave * 4 + j;           // 1 KB piece = tile rows 2q, 2q+1
+      const int r = 2 * q + (lane >> 5);
+      const int c = (lane & 31) ^ kmaj_swz(r);
+      const int m = min(m0 + c * 8, m_valid - 8);
+      row[j] = r;
+      col[j] = (uint32_t)m * 2u;
+    }
+  }
+  __device__ __forceinline__ void issue(int k0, LCE_LDS char* tile, int wave) const {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t kr = (uint32_t)min(k0 + row[j], k_last);
+      g2lds16(base + kr * ld2 + col[j], tile + (wave * 4 + j) * 1024);
+    }
+  }
 };
 
-// One K=64 stage: 4 MFMA k-steps of 16 over the wave's MI x NI accumulators.
-// With kZeroInit the first k-step starts from a literal-zero accumulator, so a
-// tile never spends instructions clearing its accumulators.
-template <int MI, int NI, bool kZeroInit>
-__device__ __forceinline__ void mma_stage(const LCE_LDS char* a_tile, const LCE_LDS char* b_tile, int a_wrow,
-                                          int b_wrow, int lane, f32x16 (&acc)[MI][NI]) {
-  const int sw = swz(lane);
-  const int half = lane >> 5;
-  const int ra = (a_wrow + (lane & 31)) * 128;
-  const int rb = (b_wrow + (lane & 31)) * 128;
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const int slot = ((ks * 2 + half) ^ sw) * 16;
-    bf16x8 a[MI], b[NI];
-#pragma unroll
-    for (int i = 0; i < MI; ++i) a[i] = *reinterpret_cast<const LCE_LDS bf16x8*>(a_tile + ra + i * 4096 + slot);
-#pragma unroll
-    for (int j = 0; j < NI; ++j) b[j] = *reinterpret_cast<const LCE_LDS bf16x8*>(b_tile + rb + j * 4096 + slot);
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        if (kZeroInit && ks == 0) {
-          const f32x16 zero = {};
-          acc[i][j] = mfma32(a[i], b[j], zero);
-        } else {
-          acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
-        }
-      }
+// ---- LDS -> register fragments --------------------------------------------
+// Fragment of block i (32 rows of the wave's sub-tile) for k-step ks: lane l
+// holds operand row (l % 32) and k = 16 ks + 8 (l / 32) + 0..7.
+
+template <int NB>
+struct KContigReader {
+  int base;  // byte offset of this lane's row in the operand tile
+  int sw;
+  __device__ __forceinline__ void init(int wrow, int lane) {
+    base = (wrow + (lane & 31)) * 128;
+    sw = swz(lane & 31);
   }
+  __device__ __forceinline__ void read(const LCE_LDS char* tile, int ks, int lane, bf16x8 (&f)[NB]) const {
+    const int slot = ((ks * 2 + (lane >> 5)) ^ sw) * 16;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) f[i] = *reinterpret_cast<const LCE_LDS bf16x8*>(tile + base + i * 4096 + slot);
+  }
+};
+
+// Transposing read of a K-major tile. ds_read_tr16_b64 works on groups of 16
+// lanes: each lane loads 4 consecutive bf16 and lane i of the group receives
+// element (i % 4) of lanes 4q + i / 4, q = 0..3. A lane at position 4q + r of
+// its group therefore loads row k = kbase + q, columns mbase + 4r .. +3, so
+// that lane i receives column mbase + i at rows kbase .. kbase + 3; two such
+// reads (k + 0..3, k + 4..7) make one 8-element fragment.
+template <int NB>
+struct KMajorReader {
+  int off[NB];  // byte offset for k-step 0, first half
+  __device__ __forceinline__ void init(int wrow, int lane) {
+    const int q = (lane & 15) >> 2, r = lane & 3;
+    const int k = 8 * (lane >> 5) + q;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int m = wrow + 32 * i + 16 * ((lane >> 4) & 1) + 4 * r;
+      off[i] = k * 512 + (((m >> 3) ^ kmaj_swz(k)) << 4) + (m & 7) * 2;
+    }
+  }
+  __device__ __forceinline__ void read(const LCE_LDS char* tile, int ks, int lane, bf16x8 (&f)[NB]) const {
+    (void)lane;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      // rows k and k + 4 have the same (k & 3), so the same swizzle
+      const bf16x4 lo = ds_read_tr16(tile + off[i] + ks * 16 * 512);
+      const bf16x4 hi = ds_read_tr16(tile + off[i] + ks * 16 * 512 + 4 * 512);
+      f[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  }
+};
+
+template <bool KMAJ, int NB>
+struct ReaderFor {
+  typedef KContigReader<NB> type;
+};
+template <int NB>
+struct ReaderFor<true, NB> {
+  typedef KMajorReader<NB> type;
+};
+
+template <int MI, int NI>
+__device__ __forceinline__ void mma_step(Acc& acc, const bf16x8 (&a)[MI], const bf16x8 (&b)[NI]) {
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
 }
 
-// Full K loop for one tile (K >= 64). If stage0_issued, the caller already
-// issued the loads of k-block 0 into stage 0. The accumulators need no
-// initialisation. On return all waves have passed a barrier and both LDS
-// stages are free.
-template <int WM, int WN>
-__device__ __forceinline__ void tile_mainloop(const OperandLoader& la, const OperandLoader& lb, int K,
-                                              LCE_LDS char* lds,
-                                              f32x16 (&acc)[TileShape<WM, WN>::kMI][TileShape<WM, WN>::kNI],
-                                              bool stage0_issued) {
-  using S = TileShape<WM, WN>;
+// Ask the scheduler to put one LDS read after each of the first n MFMAs of the
+// step, then the remaining MFMAs.
+template <int NMFMA, int NDS>
+__device__ __forceinline__ void interleave_mfma_ds() {
+#pragma unroll
+  for (int i = 0; i < NDS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  if (NMFMA > NDS) __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NDS, 0);
+}
+
+// Full K loop for one tile (K a positive multiple of 64). The accumulators are
+// zeroed here. On return every wave has passed a barrier after its last LDS
+// read, so both LDS stages are free for the caller.
+template <bool A_KMAJ, bool B_KMAJ, class LA, class LB>
+__device__ __forceinline__ void tile_mainloop(const LA& la, const LB& lb, int K, LCE_LDS char* lds, Acc& acc) {
   const int wave = wave_id();
   const int lane = lane_id();
-  const int wm = wave / WN;
-  const int wn = wave % WN;
+  const int wm = wave / kWN, wn = wave % kWN;
+  typename ReaderFor<A_KMAJ, kMI>::type ra;
+  typename ReaderFor<B_KMAJ, kNI>::type rb;
+  ra.init(wm * kWaveM, lane);
+  rb.init(wn * kWaveN, lane);
+#pragma unroll
+  for (int i = 0; i < kMI; ++i)
+#pragma unroll
+    for (int j = 0; j < kNI; ++j) acc[i][j] = f32x16{};
+  constexpr int kReads = (A_KMAJ ? 2 : 1) * kMI + (B_KMAJ ? 2 : 1) * kNI;
   const int kt_n = K / kBK;
-  if (!stage0_issued) {
-    la.issue(0, lds, wave);
-    lb.issue(0, lds + kTileBytes, wave);
-  }
+  la.issue(0, lds, wave);
+  lb.issue(0, lds + kOpBytes, wave);
   wait_vm0();
   __syncthreads();
+  bf16x8 a0[kMI], b0[kNI], a1[kMI], b1[kNI];
+  ra.read(lds, 0, lane, a0);
+  rb.read(lds + kOpBytes, 0, lane, b0);
   for (int kt = 0; kt < kt_n; ++kt) {
     LCE_LDS char* cur = lds + (kt & 1) * kStageBytes;
-    if (kt + 1 < kt_n) {
-      LCE_LDS char* nxt = lds + ((kt + 1) & 1) * kStageBytes;
+    LCE_LDS char* nxt = lds + ((kt + 1) & 1) * kStageBytes;
+    const bool more = kt + 1 < kt_n;
+    if (more) {
       la.issue((kt + 1) * kBK, nxt, wave);
-      lb.issue((kt + 1) * kBK, nxt + kTileBytes, wave);
+      lb.issue((kt + 1) * kBK, nxt + kOpBytes, wave);
     }
-    if (kt == 0)
-      mma_stage<S::kMI, S::kNI, true>(cur, cur + kTileBytes, wm * S::kWaveM, wn * S::kWaveN, lane, acc);
-    else
-      mma_stage<S::kMI, S::kNI, false>(cur, cur + kTileBytes, wm * S::kWaveM, wn * S::kWaveN, lane, acc);
+    ra.read(cur, 1, lane, a1);
+    rb.read(cur + kOpBytes, 1, lane, b1);
+    mma_step<kMI, kNI>(acc, a0, b0);
+    interleave_mfma_ds<kMI * kNI, kReads>();
+    ra.read(cur, 2, lane, a0);
+    rb.read(cur + kOpBytes, 2, lane, b0);
+    mma_step<kMI, kNI>(acc, a1, b1);
+    interleave_mfma_ds<kMI * kNI, kReads>();
+    ra.read(cur, 3, lane, a1);
+    rb.read(cur + kOpBytes, 3, lane, b1);
+    mma_step<kMI, kNI>(acc, a0, b0);
+    interleave_mfma_ds<kMI * kNI, kReads>();
+    // this wave's loads of the next stage have landed and its reads of this
+    // stage are in registers; after the barrier everyone's are
     wait_vm0();
+    wait_lgkm0();
     __syncthreads();
+    if (more) {
+      ra.read(nxt, 0, lane, a0);
+      rb.read(nxt + kOpBytes, 0, lane, b0);
+    }
+    mma_step<kMI, kNI>(acc, a1, b1);
+    if (more) interleave_mfma_ds<kMI * kNI, kReads>();
   }
 }
 
 // Row / column (within the 256x256 tile) of accumulator element e of block (i, j).
-template <int WM, int WN>
 __device__ __forceinline__ int acc_row(int wave, int lane, int i, int e) {
-  return (wave / WN) * TileShape<WM, WN>::kWaveM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+  return (wave / kWN) * kWaveM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
 }
-template <int WM, int WN>
 __device__ __forceinline__ int acc_col(int wave, int lane, int j) {
-  return (wave % WN) * TileShape<WM, WN>::kWaveN + j * 32 + (lane & 31);
+  return (wave % kWN) * kWaveN + j * 32 + (lane & 31);
 }
 
 }  // namespace lce
