@@ -102,6 +102,9 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="copy this many MiB device-to-device once before timing (a plain copy of known size, "
+                         "for scaling hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the ring across P GPUs is a "
@@ -141,6 +144,18 @@ def main() -> int:
         lce.backward(hidden, shards, targets, lse, dloss, workspace=ws, d_hidden=d_hidden, d_shards=d_shards)
         return loss
 
+    if args.copy_calibration_mib:
+        # a plain device-to-device copy of known size from a cold source: the
+        # source is written, then evicted from the caches by filling a larger
+        # buffer, then copied once
+        src = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device=dev)
+        src.fill_(1)
+        evict = torch.empty(2 * src.numel(), dtype=torch.uint8, device=dev)
+        evict.fill_(2)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        del src, dst, evict
     for _ in range(args.warmup):
         loss = step()
     torch.cuda.synchronize(dev)
