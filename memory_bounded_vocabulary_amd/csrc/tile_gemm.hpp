@@ -181,19 +181,82 @@ __device__ __forceinline__ void mma_step(Acc& acc, const bf16x8 (&a)[MI], const 
 
 // Ask the scheduler to put one LDS read after each of the first n MFMAs of the
 // step, then the remaining MFMAs.
+// Ask the scheduler to spread NVM global->LDS loads and NDS LDS reads evenly
+// over the NMFMA MFMAs of a k-step (masks: 0x008 MFMA, 0x020 global load,
+// 0x100 LDS read).
+template <int I, int NMFMA, int NVM, int NDS>
+__device__ __forceinline__ void interleave_from() {
+  if constexpr (I < NMFMA) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    constexpr int nv = NVM / NMFMA + (I < NVM % NMFMA ? 1 : 0);
+    constexpr int nd = NDS / NMFMA + (I < NDS % NMFMA ? 1 : 0);
+    if constexpr (nv > 0) __builtin_amdgcn_sched_group_barrier(0x020, nv, 0);
+    if constexpr (nd > 0) __builtin_amdgcn_sched_group_barrier(0x100, nd, 0);
+    interleave_from<I + 1, NMFMA, NVM, NDS>();
+  }
+}
 template <int NMFMA, int NDS>
 __device__ __forceinline__ void interleave_mfma_ds() {
-#pragma unroll
-  for (int i = 0; i < NDS; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  interleave_from<0, NMFMA, 0, NDS>();
+}
+template <int NMFMA, int NVM, int NDS>
+__device__ __forceinline__ void interleave_mfma_vmem_ds() {
+  interleave_from<0, NMFMA, NVM, NDS>();
+}
+
+// One stage (64 of K) of the main loop, branch-free so the scheduling
+// barriers can interleave across the whole body. On entry the fragments of
+// k-step 0 of this stage are in (a0, b0) and the stage's tiles are in LDS
+// buffer kt & 1; the next stage's tiles are in flight into the other buffer.
+// k-steps 0..2: read the next k-step's fragments while the MFMAs of the
+// current one run. Then wait for the next stage's tiles and pass a barrier
+// (after which no wave reads this stage's buffer again), and during k-step 3
+// issue the loads of stage kt + 2 into this stage's buffer (kIssue) and read
+// k-step 0 of the next stage (kNext).
+template <bool A_KMAJ, bool B_KMAJ, bool kIssue, bool kNext, class LA, class LB, class RA, class RB>
+__device__ __forceinline__ void mainloop_stage(int kt, const LA& la, const LB& lb, const RA& ra, const RB& rb,
+                                               LCE_LDS char* lds, int wave, int lane, Acc& acc, bf16x8 (&a0)[kMI],
+                                               bf16x8 (&b0)[kNI], bf16x8 (&a1)[kMI], bf16x8 (&b1)[kNI]) {
+  constexpr int kReads = (A_KMAJ ? 2 : 1) * kMI + (B_KMAJ ? 2 : 1) * kNI;
+  constexpr int kLoads = 8;  // global->LDS loads per wave per stage
+  LCE_LDS char* cur = lds + (kt & 1) * kStageBytes;
+  LCE_LDS char* nxt = lds + ((kt + 1) & 1) * kStageBytes;
+  ra.read(cur, 1, lane, a1);
+  rb.read(cur + kOpBytes, 1, lane, b1);
+  mma_step<kMI, kNI>(acc, a0, b0);
+  interleave_mfma_ds<kMI * kNI, kReads>();
+  ra.read(cur, 2, lane, a0);
+  rb.read(cur + kOpBytes, 2, lane, b0);
+  mma_step<kMI, kNI>(acc, a1, b1);
+  interleave_mfma_ds<kMI * kNI, kReads>();
+  ra.read(cur, 3, lane, a1);
+  rb.read(cur + kOpBytes, 3, lane, b1);
+  mma_step<kMI, kNI>(acc, a0, b0);
+  interleave_mfma_ds<kMI * kNI, kReads>();
+  wait_vm0();
+  wait_lgkm0();
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+  if (kIssue) {
+    la.issue((kt + 2) * kBK, cur, wave);
+    lb.issue((kt + 2) * kBK, cur + kOpBytes, wave);
   }
-  if (NMFMA > NDS) __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NDS, 0);
+  if (kNext) {
+    ra.read(nxt, 0, lane, a0);
+    rb.read(nxt + kOpBytes, 0, lane, b0);
+  }
+  mma_step<kMI, kNI>(acc, a1, b1);
+  if (kIssue && kNext) {
+    interleave_mfma_vmem_ds<kMI * kNI, kLoads, kReads>();
+  } else if (kNext) {
+    interleave_mfma_ds<kMI * kNI, kReads>();
+  }
 }
 
 // Full K loop for one tile (K a positive multiple of 64). The accumulators are
 // zeroed here. On return every wave has passed a barrier after its last LDS
-// read, so both LDS stages are free for the caller.
+// read and no load into LDS is in flight, so both LDS stages are free for the
+// caller.
 template <bool A_KMAJ, bool B_KMAJ, class LA, class LB>
 __device__ __forceinline__ void tile_mainloop(const LA& la, const LB& lb, int K, LCE_LDS char* lds, Acc& acc) {
   const int wave = wave_id();
@@ -207,47 +270,26 @@ __device__ __forceinline__ void tile_mainloop(const LA& la, const LB& lb, int K,
   for (int i = 0; i < kMI; ++i)
 #pragma unroll
     for (int j = 0; j < kNI; ++j) acc[i][j] = f32x16{};
-  constexpr int kReads = (A_KMAJ ? 2 : 1) * kMI + (B_KMAJ ? 2 : 1) * kNI;
   const int kt_n = K / kBK;
   la.issue(0, lds, wave);
   lb.issue(0, lds + kOpBytes, wave);
-  wait_vm0();
+  if (kt_n > 1) {
+    la.issue(kBK, lds + kStageBytes, wave);
+    lb.issue(kBK, lds + kStageBytes + kOpBytes, wave);
+    wait_vm<8>();  // stage 0 landed (the 8 loads of stage 1 may still fly)
+  } else {
+    wait_vm0();
+  }
   __syncthreads();
   bf16x8 a0[kMI], b0[kNI], a1[kMI], b1[kNI];
   ra.read(lds, 0, lane, a0);
   rb.read(lds + kOpBytes, 0, lane, b0);
-  for (int kt = 0; kt < kt_n; ++kt) {
-    LCE_LDS char* cur = lds + (kt & 1) * kStageBytes;
-    LCE_LDS char* nxt = lds + ((kt + 1) & 1) * kStageBytes;
-    const bool more = kt + 1 < kt_n;
-    if (more) {
-      la.issue((kt + 1) * kBK, nxt, wave);
-      lb.issue((kt + 1) * kBK, nxt + kOpBytes, wave);
-    }
-    ra.read(cur, 1, lane, a1);
-    rb.read(cur + kOpBytes, 1, lane, b1);
-    mma_step<kMI, kNI>(acc, a0, b0);
-    interleave_mfma_ds<kMI * kNI, kReads>();
-    ra.read(cur, 2, lane, a0);
-    rb.read(cur + kOpBytes, 2, lane, b0);
-    mma_step<kMI, kNI>(acc, a1, b1);
-    interleave_mfma_ds<kMI * kNI, kReads>();
-    ra.read(cur, 3, lane, a1);
-    rb.read(cur + kOpBytes, 3, lane, b1);
-    mma_step<kMI, kNI>(acc, a0, b0);
-    interleave_mfma_ds<kMI * kNI, kReads>();
-    // this wave's loads of the next stage have landed and its reads of this
-    // stage are in registers; after the barrier everyone's are
-    wait_vm0();
-    wait_lgkm0();
-    __syncthreads();
-    if (more) {
-      ra.read(nxt, 0, lane, a0);
-      rb.read(nxt + kOpBytes, 0, lane, b0);
-    }
-    mma_step<kMI, kNI>(acc, a1, b1);
-    if (more) interleave_mfma_ds<kMI * kNI, kReads>();
-  }
+  int kt = 0;
+  for (; kt < kt_n - 2; ++kt)
+    mainloop_stage<A_KMAJ, B_KMAJ, true, true>(kt, la, lb, ra, rb, lds, wave, lane, acc, a0, b0, a1, b1);
+  if (kt_n >= 2)
+    mainloop_stage<A_KMAJ, B_KMAJ, false, true>(kt_n - 2, la, lb, ra, rb, lds, wave, lane, acc, a0, b0, a1, b1);
+  mainloop_stage<A_KMAJ, B_KMAJ, false, false>(kt_n - 1, la, lb, ra, rb, lds, wave, lane, acc, a0, b0, a1, b1);
 }
 
 // Row / column (within the 256x256 tile) of accumulator element e of block (i, j).
