@@ -97,8 +97,11 @@ Plan make_plan(const lce_dims* d) {
   p.n_pad = round_up(p.N, kTile);
   p.token_blocks = p.n_pad / kTile;
   p.vocab_tiles = ceil_div(p.Vs, kTile);
-  // Split each shard's vocabulary tiles until the grid has about one workgroup per CU.
-  int64_t s = std::min<int64_t>({kMaxSplits, p.vocab_tiles, std::max<int64_t>(1, ceil_div(kTargetWorkgroups, p.token_blocks))});
+  // Split each shard's vocabulary tiles: at least 8 ways (the XCD-grouped
+  // tile order puts 4 token blocks x 8 splits on an XCD at once), more while
+  // the grid would not give every CU a workgroup.
+  int64_t s = std::min<int64_t>(
+      {kMaxSplits, p.vocab_tiles, std::max<int64_t>(8, ceil_div(kTargetWorkgroups, p.token_blocks))});
   p.tiles_per_split = ceil_div(p.vocab_tiles, s);
   p.splits = ceil_div(p.vocab_tiles, p.tiles_per_split);
   // Backward chunks: balanced, tile-aligned, bounded by constants.

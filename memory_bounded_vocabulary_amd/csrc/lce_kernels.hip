@@ -24,9 +24,9 @@ namespace lce {
 // token therefore lives in two registers per lane and the fold needs no
 // cross-lane traffic until the very end.
 //
-// Grid (token blocks, S splits). Workgroup (tb, s) owns tokens [256 tb, 256 tb
-// + 256) and the vocabulary tiles [s*tps, min((s+1)*tps, n_vtiles)) of the
-// shard. Its (m, z) per token is merged, in a fixed order, into state[s][token]
+// Grid: token blocks x S splits, in the XCD-grouped order of xcd_tile.
+// Workgroup (tb, s) owns tokens [256 tb, 256 tb + 256) and the vocabulary
+// tiles [s*tps, min((s+1)*tps, n_vtiles)) of the shard. Its (m, z) per token is merged, in a fixed order, into state[s][token]
 // once per round, so over the rounds each split meets the shards in ring
 // order. Every (s, token) has exactly one writer per launch and launches are
 // ordered on the stream: no atomics, bitwise-reproducible.
@@ -79,14 +79,15 @@ __device__ __forceinline__ void fold_masked(const Acc& acc, float (&m)[kNI], flo
 __global__ __launch_bounds__(kThreads, 1) void fwd_round_kernel(const uint16_t* __restrict__ X, int N, int H,
                                                                 const uint16_t* __restrict__ W, int Vs,
                                                                 float2* __restrict__ state, int state_ld,
-                                                                int tiles_per_split, int n_vtiles, int first) {
+                                                                int token_blocks, int S, int tiles_per_split,
+                                                                int n_vtiles, int first) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[kMainLds];
   LCE_LDS char* lds = (LCE_LDS char*)lds_raw;
   const int wave = wave_id();
   const int lane = lane_id();
   const int wm = wave / kWN, wn = wave % kWN;
-  const int tb = blockIdx.x;
-  const int split = blockIdx.y;
+  int tb, split;
+  xcd_tile(blockIdx.x, token_blocks, S, tb, split);
   const int t0 = split * tiles_per_split;
   const int t1 = min(t0 + tiles_per_split, n_vtiles);
 
@@ -281,13 +282,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_g_kernel(const uint16_t* __re
                                                             const float* __restrict__ lse,
                                                             const float* __restrict__ gscale, int ignore_index,
                                                             int vocab_base, int V, uint16_t* __restrict__ G,
-                                                            int ldg) {
+                                                            int ldg, int n_tt, int n_tv) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[kMainLds];
   LCE_LDS char* lds = (LCE_LDS char*)lds_raw;
   const int wave = wave_id();
   const int lane = lane_id();
   const int wm = wave / kWN, wn = wave % kWN;
-  const int tv = blockIdx.x, tt = blockIdx.y;
+  int tt, tv;
+  xcd_tile(blockIdx.x, n_tt, n_tv, tt, tv);
 
   // per-lane token info: log2-domain lse, gradient scale, target row in this tile
   float lse2[kNI], g[kNI];
@@ -354,8 +356,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_g_kernel(const uint16_t* __re
 // --------------------------------------------------------------------------
 // Both gradient contractions of one (token chunk, vocabulary chunk) block in
 // one launch, each 256 x 256 output tile a workgroup:
-//   tiles [0, dx_tiles):   dX[n0 + m][h]  (+)= sum_v G[m][v] W_s[v0 + v][h]
-//   tiles [dx_tiles, ..):  dW_s[v0 + m][h] (+)= sum_t G[t][m] X[n0 + t][h]
+//   dX[n0 + m][h]   (+)= sum_v G[m][v] W_s[v0 + v][h]   (K = vc_pad)
+//   dW_s[v0 + m][h] (+)= sum_t G[t][m] X[n0 + t][h]     (K = nc_pad)
+// The problem with the longer K takes the first workgroups (padded to a
+// multiple of 8 so both problems start on XCD 0), so the long tiles are
+// dispatched first and the short ones fill in behind them; within each
+// problem the tiles follow the XCD-grouped order of xcd_tile.
 // G is read as it was written: K-contiguous for dX, K-major for dW; W_s and X
 // are K-major for both. Output tiles are stored (or added) in fp32.
 // --------------------------------------------------------------------------
@@ -382,16 +388,28 @@ __global__ __launch_bounds__(kThreads, 1) void grad_gemm_kernel(const uint16_t* 
                                                                 int vc_pad, const uint16_t* __restrict__ Wc, int vc,
                                                                 const uint16_t* __restrict__ Xc, int nc, int H,
                                                                 float* __restrict__ dX, int acc_dx,
-                                                                float* __restrict__ dW, int acc_dw, int dx_tiles,
-                                                                int n_tiles) {
+                                                                float* __restrict__ dW, int acc_dw, int n_tiles,
+                                                                int dw_first, int first_slots) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[kMainLds];
   LCE_LDS char* lds = (LCE_LDS char*)lds_raw;
   const int wave = wave_id();
   const int lane = lane_id();
+  const int dx_rows = nc_pad / kBM, dw_rows = vc_pad / kBM;
   int id = blockIdx.x;
+  bool is_dx;
+  int rows;
+  if (id < first_slots) {
+    is_dx = !dw_first;
+  } else {
+    is_dx = dw_first;
+    id -= first_slots;
+  }
+  rows = is_dx ? dx_rows : dw_rows;
+  if (id >= rows * n_tiles) return;  // padding slot
+  int tm, tn;
+  xcd_tile(id, rows, n_tiles, tm, tn);
   Acc acc;
-  if (id < dx_tiles) {
-    const int tm = id / n_tiles, tn = id % n_tiles;
+  if (is_dx) {
     KContigLoader la;
     KMajorLoader lb;
     la.init(G, ldg, tm * kBM, nc_pad, wave, lane);
@@ -399,8 +417,6 @@ __global__ __launch_bounds__(kThreads, 1) void grad_gemm_kernel(const uint16_t* 
     tile_mainloop<false, true>(la, lb, vc_pad, lds, acc);
     store_tile(acc, dX, H, tm * kBM, nc, tn * kBN, H, acc_dx, wave, lane);
   } else {
-    id -= dx_tiles;
-    const int tm = id / n_tiles, tn = id % n_tiles;
     KMajorLoader la, lb;
     la.init(G, ldg, tm * kBM, vc_pad, nc_pad, wave, lane);
     lb.init(Xc, H, tn * kBN, H, nc, wave, lane);
@@ -414,8 +430,8 @@ static inline hipError_t last() { return hipGetLastError(); }
 
 hipError_t launch_fwd_round(const uint16_t* X, int N, int H, const uint16_t* W, int Vs, float2* state, int state_ld,
                             int token_blocks, int S, int tiles_per_split, int n_vtiles, int first, hipStream_t st) {
-  hipLaunchKernelGGL(fwd_round_kernel, dim3(token_blocks, S), dim3(kThreads), 0, st, X, N, H, W, Vs, state, state_ld,
-                     tiles_per_split, n_vtiles, first);
+  hipLaunchKernelGGL(fwd_round_kernel, dim3(token_blocks * S), dim3(kThreads), 0, st, X, N, H, W, Vs, state,
+                     state_ld, token_blocks, S, tiles_per_split, n_vtiles, first);
   return last();
 }
 
@@ -447,8 +463,9 @@ hipError_t launch_bwd_scale(const int* targets, int N, int ignore_index, const f
 hipError_t launch_bwd_g(const uint16_t* X, int N, int H, const uint16_t* Ws, int Vs, int v0, int vc, int n0, int nc,
                         const int* targets, const float* lse, const float* gscale, int ignore_index, int vocab_base,
                         int V, uint16_t* G, int ldg, int nc_pad, int vc_pad, hipStream_t st) {
-  hipLaunchKernelGGL(bwd_g_kernel, dim3(vc_pad / kBM, nc_pad / kBN), dim3(kThreads), 0, st, X, N, H, Ws, Vs, v0, vc,
-                     n0, nc, targets, lse, gscale, ignore_index, vocab_base, V, G, ldg);
+  const int n_tt = nc_pad / kBN, n_tv = vc_pad / kBM;
+  hipLaunchKernelGGL(bwd_g_kernel, dim3(n_tt * n_tv), dim3(kThreads), 0, st, X, N, H, Ws, Vs, v0, vc, n0, nc, targets,
+                     lse, gscale, ignore_index, vocab_base, V, G, ldg, n_tt, n_tv);
   return last();
 }
 
@@ -458,8 +475,11 @@ hipError_t launch_grad_gemm(const uint16_t* G, int ldg, int nc_pad, int vc_pad, 
   const int n_tiles = H / kBN + (H % kBN ? 1 : 0);
   const int dx_tiles = (nc_pad / kBM) * n_tiles;
   const int dw_tiles = (vc_pad / kBM) * n_tiles;
-  hipLaunchKernelGGL(grad_gemm_kernel, dim3(dx_tiles + dw_tiles), dim3(kThreads), 0, st, G, ldg, nc_pad, vc_pad, Wc,
-                     vc, Xc, nc, H, dX, acc_dx, dW, acc_dw, dx_tiles, n_tiles);
+  const int dw_first = nc_pad > vc_pad ? 1 : 0;  // dW tiles have K = nc_pad, dX tiles K = vc_pad
+  const int first = dw_first ? dw_tiles : dx_tiles, second = dw_first ? dx_tiles : dw_tiles;
+  const int first_slots = (first + 7) & ~7;
+  hipLaunchKernelGGL(grad_gemm_kernel, dim3(first_slots + second), dim3(kThreads), 0, st, G, ldg, nc_pad, vc_pad, Wc,
+                     vc, Xc, nc, H, dX, acc_dx, dW, acc_dw, n_tiles, dw_first, first_slots);
   return last();
 }
 

@@ -292,6 +292,26 @@ __device__ __forceinline__ void tile_mainloop(const LA& la, const LB& lb, int K,
   mainloop_stage<A_KMAJ, B_KMAJ, false, false>(kt_n - 1, la, lb, ra, rb, lds, wave, lane, acc, a0, b0, a1, b1);
 }
 
+// Tile (r, c) of workgroup b within a problem of rows x cols tiles occupying
+// workgroups [0, rows * cols) of a launch. The hardware hands workgroups to the
+// eight XCDs round-robin (b % 8), and each XCD has its own L2. Here each XCD
+// gets a contiguous run of the tile order, which walks bands of kBand rows
+// column by column, so the 32 workgroups an XCD runs at once cover a
+// kBand x 8 rectangle and share 4 + 8 operand tiles instead of up to 64.
+constexpr int kBand = 4;
+__device__ __forceinline__ void xcd_tile(int b, int rows, int cols, int& r, int& c) {
+  const int n = rows * cols;
+  const int x = b & 7, l = b >> 3;
+  const int q = n >> 3, rem = n & 7;
+  const int t = x * q + min(x, rem) + l;
+  const int band = t / (kBand * cols);
+  const int r0 = band * kBand;
+  const int h = min(rows - r0, kBand);
+  const int w = t - band * kBand * cols;
+  r = r0 + w % h;
+  c = w / h;
+}
+
 // Row / column (within the 256x256 tile) of accumulator element e of block (i, j).
 __device__ __forceinline__ int acc_row(int wave, int lane, int i, int e) {
   return (wave / kWN) * kWaveM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
