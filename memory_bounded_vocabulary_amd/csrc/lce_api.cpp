@@ -6,11 +6,12 @@
 //   forward   target logits; round k = 0..P-1 folds shard order[k] into the
 //             per-token running (m, z); finalize lse = m + log z, the token
 //             losses and the loss.
-//   backward  g = dloss / n_valid; then for every shard in ring order and
-//             every (vocabulary chunk, token chunk): recompute the logit block
-//             from lse and form G in bf16, then, in one launch, dX += G W_chunk
-//             and dW_chunk += G^T X_chunk (fp32). The GEMMs read W, X and G as
-//             they lie in memory; nothing is transposed.
+//   backward  g = dloss / n_valid; then for every unit (shard in ring order,
+//             vocabulary chunk, token chunk): recompute the logit block from
+//             lse and form G in bf16, then dX += G W_chunk and dW_chunk +=
+//             G^T X_chunk (fp32). One launch runs the GEMMs of unit j - 1 with
+//             the recompute of unit j (two G buffers alternate). The GEMMs
+//             read W, X and G as they lie in memory; nothing is transposed.
 // Transient device memory is O(N) plus fixed-size chunks: no logit strip
 // (N x V/P) is ever formed.
 #include <hip/hip_runtime.h>
@@ -59,7 +60,7 @@ struct Plan {
   // forward workspace
   size_t off_state, off_yt, off_part, off_nvalid, fwd_bytes;
   // backward workspace
-  size_t off_gscale, off_g, bwd_bytes;
+  size_t off_gscale, off_g, g_bytes, bwd_bytes;
   size_t bytes;
 };
 
@@ -123,8 +124,9 @@ Plan make_plan(const lce_dims* d) {
   o = 0;
   p.off_gscale = o;
   o = align256(o + 16);
-  p.off_g = o;
-  o = align256(o + size_t(p.ncs) * p.vcs * 2);
+  p.g_bytes = align256(size_t(p.ncs) * p.vcs * 2);
+  p.off_g = o;  // two G chunks: consecutive backward units alternate
+  o += 2 * p.g_bytes;
   p.bwd_bytes = o;
   p.bytes = std::max(p.fwd_bytes, p.bwd_bytes);
   return p;
@@ -170,8 +172,9 @@ int hip_status(hipError_t e, const char* what) {
 }
 
 // ---- optional per-launch event trace (see lce_trace_enable) ----
-enum Kind { kTargetLogit, kFwdRound, kFinalize, kBwdScale, kBwdG, kGradGemm, kKinds };
-const char* const kKindName[kKinds] = {"target_logit", "fwd_round", "finalize", "bwd_scale", "bwd_g", "grad_gemm"};
+enum Kind { kTargetLogit, kFwdRound, kFinalize, kBwdScale, kBwdG, kBwdStep, kGradGemm, kKinds };
+const char* const kKindName[kKinds] = {"target_logit", "fwd_round", "finalize", "bwd_scale", "bwd_g", "bwd_step",
+                                       "grad_gemm"};
 
 struct Trace {
   std::vector<hipEvent_t> ev;  // pairs: [2i] before, [2i+1] after launch i
@@ -284,7 +287,6 @@ int lce_backward(const lce_dims* d, const void* hidden, const void* const* w_sha
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   float* gscale = reinterpret_cast<float*>(ws + p.off_gscale);
-  uint16_t* G = reinterpret_cast<uint16_t*>(ws + p.off_g);
   const uint16_t* X = static_cast<const uint16_t*>(hidden);
   const int N = int(p.N), H = int(p.H), Vs = int(p.Vs), V = int(p.V);
 
@@ -293,39 +295,78 @@ int lce_backward(const lce_dims* d, const void* hidden, const void* const* w_sha
                          [&] { return lce::launch_bwd_scale(targets, N, d->ignore_index, dloss, d->reduction, gscale, s); }),
                   "scale");
   if (st) return st;
-  for (int k = 0; k < d->n_shards; ++k) {
-    const int sh = order[k];
-    const uint16_t* W = static_cast<const uint16_t*>(w_shards[sh]);
-    float* dW = d_w_shards[sh];
+  // Backward units in ring order: (shard, vocabulary chunk, token chunk).
+  // Launch j runs the gradient GEMMs of unit j - 1 and the recompute of unit j.
+  struct Unit {
+    int sh, v0, vc, vc_pad, n0, nc, nc_pad;
+  };
+  std::vector<Unit> units;
+  for (int k = 0; k < d->n_shards; ++k)
     for (int64_t v0 = 0; v0 < p.Vs; v0 += p.vcs) {
       const int vc = int(std::min<int64_t>(p.vcs, p.Vs - v0));
-      const int vc_pad = int(round_up(vc, kTile));
-      const double dvc = double(vc);
       for (int64_t n0 = 0; n0 < p.N; n0 += p.ncs) {
         const int nc = int(std::min<int64_t>(p.ncs, p.N - n0));
-        const int nc_pad = int(round_up(nc, kTile));
-        const double dnc = double(nc), dgb = 2.0 * double(nc_pad) * double(vc_pad);
-        st = hip_status(traced(kBwdG, 2.0 * dnc * dvc * dH, 2.0 * dnc * dH + 2.0 * dvc * dH + dgb + 12.0 * dnc, s,
-                               [&] {
-                                 return lce::launch_bwd_g(X, N, H, W, Vs, int(v0), vc, int(n0), nc, targets, lse,
-                                                          gscale, d->ignore_index, int(sh * p.Vs + v0), V, G, vc_pad,
-                                                          nc_pad, vc_pad, s);
-                               }),
-                        "gradient block");
-        if (st) return st;
-        const int acc_dx = (k > 0 || v0 > 0) ? 1 : 0, acc_dw = n0 > 0 ? 1 : 0;
-        const double bytes = 2.0 * dgb + 2.0 * dvc * dH + 2.0 * dnc * dH + (4.0 + 4.0 * acc_dx) * dnc * dH +
-                             (4.0 + 4.0 * acc_dw) * dvc * dH;
-        st = hip_status(traced(kGradGemm, 4.0 * dnc * dvc * dH, bytes, s,
-                               [&] {
-                                 return lce::launch_grad_gemm(G, vc_pad, nc_pad, vc_pad, W + v0 * p.H, vc,
-                                                              X + n0 * p.H, nc, H, d_hidden + n0 * p.H, acc_dx,
-                                                              dW + v0 * p.H, acc_dw, s);
-                               }),
-                        "dX and dW");
-        if (st) return st;
+        units.push_back({order[k], int(v0), vc, int(round_up(vc, kTile)), int(n0), nc, int(round_up(nc, kTile))});
       }
     }
+  auto gbuf = [&](size_t u) { return reinterpret_cast<uint16_t*>(ws + p.off_g + (u & 1) * p.g_bytes); };
+  std::vector<bool> dx_written(size_t(ceil_div(p.N, p.ncs)), false);
+  for (size_t j = 0; j <= units.size(); ++j) {
+    lce::GradArgs ga{};
+    lce::BwdGArgs ba{};
+    double flops = 0.0, bytes = 0.0;
+    if (j > 0) {
+      const Unit& u = units[j - 1];
+      const size_t nchunk = size_t(u.n0 / p.ncs);
+      ga.G = gbuf(j - 1);
+      ga.ldg = u.vc_pad;
+      ga.nc_pad = u.nc_pad;
+      ga.vc_pad = u.vc_pad;
+      ga.Wc = static_cast<const uint16_t*>(w_shards[u.sh]) + size_t(u.v0) * p.H;
+      ga.vc = u.vc;
+      ga.Xc = X + size_t(u.n0) * p.H;
+      ga.nc = u.nc;
+      ga.H = H;
+      ga.dX = d_hidden + size_t(u.n0) * p.H;
+      ga.acc_dx = dx_written[nchunk] ? 1 : 0;
+      dx_written[nchunk] = true;
+      ga.dW = d_w_shards[u.sh] + size_t(u.v0) * p.H;
+      ga.acc_dw = u.n0 > 0 ? 1 : 0;
+      const double dnc = u.nc, dvc = u.vc, gb = 2.0 * double(u.nc_pad) * double(u.vc_pad);
+      flops += 4.0 * dnc * dvc * dH;
+      bytes += 2.0 * gb + 2.0 * dvc * dH + 2.0 * dnc * dH + (4.0 + 4.0 * ga.acc_dx) * dnc * dH +
+               (4.0 + 4.0 * ga.acc_dw) * dvc * dH;
+    }
+    if (j < units.size()) {
+      const Unit& u = units[j];
+      ba.X = X;
+      ba.Ws = static_cast<const uint16_t*>(w_shards[u.sh]);
+      ba.targets = targets;
+      ba.lse = lse;
+      ba.gscale = gscale;
+      ba.G = gbuf(j);
+      ba.N = N;
+      ba.H = H;
+      ba.Vs = Vs;
+      ba.v0 = u.v0;
+      ba.vc = u.vc;
+      ba.n0 = u.n0;
+      ba.nc = u.nc;
+      ba.nc_pad = u.nc_pad;
+      ba.vc_pad = u.vc_pad;
+      ba.ignore_index = d->ignore_index;
+      ba.vocab_base = int(u.sh * p.Vs + u.v0);
+      ba.V = V;
+      ba.ldg = u.vc_pad;
+      const double dnc = u.nc, dvc = u.vc;
+      flops += 2.0 * dnc * dvc * dH;
+      bytes += 2.0 * dnc * dH + 2.0 * dvc * dH + 2.0 * double(u.nc_pad) * double(u.vc_pad) + 12.0 * dnc;
+    }
+    const Kind kind = j == 0 ? kBwdG : (j == units.size() ? kGradGemm : kBwdStep);
+    st = hip_status(traced(kind, flops, bytes, s,
+                           [&] { return lce::launch_bwd_step(j > 0 ? &ga : nullptr, j < units.size() ? &ba : nullptr, s); }),
+                    "backward step");
+    if (st) return st;
   }
   return LCE_OK;
 }

@@ -23,11 +23,32 @@ hipError_t launch_finalize(const float2* state, int state_ld, int S, const float
                            float* loss, float* n_valid_out, hipStream_t st);
 hipError_t launch_bwd_scale(const int* targets, int N, int ignore_index, const float* dloss, int reduction,
                             float* gscale, hipStream_t st);
-hipError_t launch_bwd_g(const uint16_t* X, int N, int H, const uint16_t* Ws, int Vs, int v0, int vc, int n0, int nc,
-                        const int* targets, const float* lse, const float* gscale, int ignore_index, int vocab_base,
-                        int V, uint16_t* G, int ldg, int nc_pad, int vc_pad, hipStream_t st);
-hipError_t launch_grad_gemm(const uint16_t* G, int ldg, int nc_pad, int vc_pad, const uint16_t* Wc, int vc,
-                            const uint16_t* Xc, int nc, int H, float* dX, int acc_dx, float* dW, int acc_dw,
-                            hipStream_t st);
+// Recompute + G of one backward unit (shard, vocabulary chunk, token chunk).
+struct BwdGArgs {
+  const uint16_t* X;        // hidden [N][H]
+  const uint16_t* Ws;       // the unit's shard [Vs][H]
+  const int* targets;
+  const float* lse;
+  const float* gscale;      // device scalar g = dloss / n_valid (or dloss)
+  uint16_t* G;              // [nc_pad][vc_pad], pitch ldg
+  int N, H, Vs, v0, vc, n0, nc, nc_pad, vc_pad;
+  int ignore_index, vocab_base, V, ldg;
+  int n_tt, n_tv;           // set by the launcher
+};
+
+// The two gradient contractions of one backward unit.
+struct GradArgs {
+  const uint16_t* G;        // [nc_pad][vc_pad], pitch ldg
+  const uint16_t* Wc;       // shard rows v0.. [vc][H]
+  const uint16_t* Xc;       // hidden rows n0.. [nc][H]
+  float* dX;                // d_hidden rows n0..
+  float* dW;                // d_shard rows v0..
+  int ldg, nc_pad, vc_pad, vc, nc, H, acc_dx, acc_dw;
+  int n_tiles, dw_first, first_slots;  // set by the launcher
+};
+
+// One launch: the gradient tiles of `gr` (may be NULL) and the recompute tiles
+// of `bg` (may be NULL); their G buffers must differ.
+hipError_t launch_bwd_step(const GradArgs* gr, const BwdGArgs* bg, hipStream_t st);
 
 }  // namespace lce

@@ -265,31 +265,37 @@ __global__ __launch_bounds__(256) void bwd_scale_kernel(const int* __restrict__ 
 }
 
 // --------------------------------------------------------------------------
-// Backward recompute of one 256 x 256 block of the (token chunk, vocabulary
-// chunk) logits and its gradient G = g_i (exp(y - lse_i) - [v == t_i]) in bf16
+// Backward, one unit = (shard, vocabulary chunk, token chunk).
+//
+// recompute_g_tile: one 256 x 256 block of the unit's logits, recomputed from
+// X and W_s, and its gradient G = g_i (exp(y - lse_i) - [v == t_i]) in bf16
 // (round to nearest even), written to G [token][vocabulary] (row pitch ldg).
-// As in the forward, the tile is computed vocabulary x token, so each lane
-// owns two token columns and their (lse, g, target) sit in registers. Rows
-// past the token chunk (g = 0, lse = +inf) and columns past the vocabulary
-// chunk are written as 0, so G is a dense zero-padded [nc_pad][vc_pad] matrix.
-// The tile is staged in LDS (16-byte chunks of each token row XOR-swizzled by
-// the row) and written out with 16-byte stores.
+// As in the forward the tile is computed vocabulary x token, so each lane owns
+// two token columns and their (lse, g, target) sit in registers. Rows past the
+// token chunk (g = 0, lse = +inf) and columns past the vocabulary chunk are
+// written as 0, so G is a dense zero-padded [nc_pad][vc_pad] matrix. The tile
+// is staged in LDS (16-byte chunks of each token row XOR-swizzled by the row)
+// and written out with 16-byte stores.
+//
+// grad_tile: one 256 x 256 output tile of the unit's two contractions
+//   dX[n0 + m][h]   (+)= sum_v G[m][v] W_s[v0 + v][h]   (K = vc_pad)
+//   dW_s[v0 + m][h] (+)= sum_t G[t][m] X[n0 + t][h]     (K = nc_pad)
+// G is read as it was written: K-contiguous for dX, K-major for dW; W_s and X
+// are K-major for both. The problem with the longer K takes the first slots
+// (padded to a multiple of 8 so both start on XCD 0) so the long tiles are
+// dispatched first; within each problem the tiles follow xcd_tile.
+//
+// bwd_step_kernel runs, in one launch, the gradient tiles of unit u - 1 (first
+// slots) and the recompute tiles of unit u (after them), with the two units'
+// G in different buffers: the short recompute tiles fill in behind the long
+// gradient tiles, and the backward needs one launch per unit instead of two.
 // --------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads, 1) void bwd_g_kernel(const uint16_t* __restrict__ X, int N, int H,
-                                                            const uint16_t* __restrict__ Ws, int Vs, int v0,
-                                                            int vc, int n0, int nc,
-                                                            const int* __restrict__ targets,
-                                                            const float* __restrict__ lse,
-                                                            const float* __restrict__ gscale, int ignore_index,
-                                                            int vocab_base, int V, uint16_t* __restrict__ G,
-                                                            int ldg, int n_tt, int n_tv) {
-  __shared__ __attribute__((aligned(1024))) char lds_raw[kMainLds];
-  LCE_LDS char* lds = (LCE_LDS char*)lds_raw;
+__device__ __forceinline__ void recompute_g_tile(const BwdGArgs& a, int id, LCE_LDS char* lds, char* ldsg) {
   const int wave = wave_id();
   const int lane = lane_id();
   const int wm = wave / kWN, wn = wave % kWN;
   int tt, tv;
-  xcd_tile(blockIdx.x, n_tt, n_tv, tt, tv);
+  xcd_tile(id, a.n_tt, a.n_tv, tt, tv);
 
   // per-lane token info: log2-domain lse, gradient scale, target row in this tile
   float lse2[kNI], g[kNI];
@@ -297,30 +303,30 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_g_kernel(const uint16_t* __re
 #pragma unroll
   for (int j = 0; j < kNI; ++j) {
     const int rr = tt * kBN + wn * kWaveN + 32 * j + (lane & 31);
-    const int row = n0 + rr;
+    const int row = a.n0 + rr;
     lse2[j] = __builtin_inff();
     g[j] = 0.0f;
     tcol[j] = -1;
-    if (rr < nc && row < N) {
-      lse2[j] = lse[row] * kLog2e;
-      const int t = targets[row];
-      if (t != ignore_index) {
-        if (t < 0 || t >= V) {
+    if (rr < a.nc && row < a.N) {
+      lse2[j] = a.lse[row] * kLog2e;
+      const int t = a.targets[row];
+      if (t != a.ignore_index) {
+        if (t < 0 || t >= a.V) {
           g[j] = __builtin_nanf("");
         } else {
-          g[j] = gscale[0];
-          tcol[j] = t - (vocab_base + tv * kBM);
+          g[j] = a.gscale[0];
+          tcol[j] = t - (a.vocab_base + tv * kBM);
         }
       }
     }
   }
   KContigLoader lw, lx;
-  lw.init(Ws, H, v0 + tv * kBM, Vs, wave, lane);
-  lx.init(X, H, n0 + tt * kBN, N, wave, lane);
+  lw.init(a.Ws, a.H, a.v0 + tv * kBM, a.Vs, wave, lane);
+  lx.init(a.X, a.H, a.n0 + tt * kBN, a.N, wave, lane);
   Acc acc;
-  tile_mainloop<false, false>(lw, lx, H, lds, acc);
+  tile_mainloop<false, false>(lw, lx, a.H, lds, acc);
 
-  const int live = vc - tv * kBM;  // vocabulary rows of this tile inside the chunk
+  const int live = a.vc - tv * kBM;  // vocabulary rows of this tile inside the chunk
 #pragma unroll
   for (int j = 0; j < kNI; ++j) {
     const int tok = wn * kWaveN + 32 * j + (lane & 31);  // token row of the staged tile
@@ -339,32 +345,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_g_kernel(const uint16_t* __re
         }
         const int slot = (r0 >> 3) ^ (tok & 31);
         uint2 packed = make_uint2(pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3]));
-        *reinterpret_cast<uint2*>(lds_raw + tok * 512 + slot * 16 + (r0 & 7) * 2) = packed;
+        *reinterpret_cast<uint2*>(ldsg + tok * 512 + slot * 16 + (r0 & 7) * 2) = packed;
       }
   }
   __syncthreads();
-  uint16_t* gt = G + (size_t)tt * kBN * ldg + (size_t)tv * kBM;
+  uint16_t* gt = a.G + (size_t)tt * kBN * a.ldg + (size_t)tv * kBM;
 #pragma unroll 4
   for (int it = 0; it < kBN * kBM / 8 / kThreads; ++it) {
     const int q = it * kThreads + threadIdx.x;
     const int r = q >> 5, c = q & 31;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(lds_raw + r * 512 + ((c ^ (r & 31)) << 4));
-    *reinterpret_cast<u32x4*>(gt + (size_t)r * ldg + c * 8) = v;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(ldsg + r * 512 + ((c ^ (r & 31)) << 4));
+    *reinterpret_cast<u32x4*>(gt + (size_t)r * a.ldg + c * 8) = v;
   }
 }
 
-// --------------------------------------------------------------------------
-// Both gradient contractions of one (token chunk, vocabulary chunk) block in
-// one launch, each 256 x 256 output tile a workgroup:
-//   dX[n0 + m][h]   (+)= sum_v G[m][v] W_s[v0 + v][h]   (K = vc_pad)
-//   dW_s[v0 + m][h] (+)= sum_t G[t][m] X[n0 + t][h]     (K = nc_pad)
-// The problem with the longer K takes the first workgroups (padded to a
-// multiple of 8 so both problems start on XCD 0), so the long tiles are
-// dispatched first and the short ones fill in behind them; within each
-// problem the tiles follow the XCD-grouped order of xcd_tile.
-// G is read as it was written: K-contiguous for dX, K-major for dW; W_s and X
-// are K-major for both. Output tiles are stored (or added) in fp32.
-// --------------------------------------------------------------------------
 __device__ __forceinline__ void store_tile(const Acc& acc, float* __restrict__ C, int ldc, int m0, int m_valid,
                                            int n0, int n_valid, int accumulate, int wave, int lane) {
 #pragma unroll
@@ -384,44 +378,47 @@ __device__ __forceinline__ void store_tile(const Acc& acc, float* __restrict__ C
     }
 }
 
-__global__ __launch_bounds__(kThreads, 1) void grad_gemm_kernel(const uint16_t* __restrict__ G, int ldg, int nc_pad,
-                                                                int vc_pad, const uint16_t* __restrict__ Wc, int vc,
-                                                                const uint16_t* __restrict__ Xc, int nc, int H,
-                                                                float* __restrict__ dX, int acc_dx,
-                                                                float* __restrict__ dW, int acc_dw, int n_tiles,
-                                                                int dw_first, int first_slots) {
-  __shared__ __attribute__((aligned(1024))) char lds_raw[kMainLds];
-  LCE_LDS char* lds = (LCE_LDS char*)lds_raw;
+__device__ __forceinline__ void grad_tile(const GradArgs& a, int id, LCE_LDS char* lds) {
   const int wave = wave_id();
   const int lane = lane_id();
-  const int dx_rows = nc_pad / kBM, dw_rows = vc_pad / kBM;
-  int id = blockIdx.x;
+  const int dx_rows = a.nc_pad / kBM, dw_rows = a.vc_pad / kBM;
   bool is_dx;
-  int rows;
-  if (id < first_slots) {
-    is_dx = !dw_first;
+  if (id < a.first_slots) {
+    is_dx = !a.dw_first;
   } else {
-    is_dx = dw_first;
-    id -= first_slots;
+    is_dx = a.dw_first;
+    id -= a.first_slots;
   }
-  rows = is_dx ? dx_rows : dw_rows;
-  if (id >= rows * n_tiles) return;  // padding slot
+  const int rows = is_dx ? dx_rows : dw_rows;
+  if (id >= rows * a.n_tiles) return;  // padding slot
   int tm, tn;
-  xcd_tile(id, rows, n_tiles, tm, tn);
+  xcd_tile(id, rows, a.n_tiles, tm, tn);
   Acc acc;
   if (is_dx) {
     KContigLoader la;
     KMajorLoader lb;
-    la.init(G, ldg, tm * kBM, nc_pad, wave, lane);
-    lb.init(Wc, H, tn * kBN, H, vc, wave, lane);
-    tile_mainloop<false, true>(la, lb, vc_pad, lds, acc);
-    store_tile(acc, dX, H, tm * kBM, nc, tn * kBN, H, acc_dx, wave, lane);
+    la.init(a.G, a.ldg, tm * kBM, a.nc_pad, wave, lane);
+    lb.init(a.Wc, a.H, tn * kBN, a.H, a.vc, wave, lane);
+    tile_mainloop<false, true>(la, lb, a.vc_pad, lds, acc);
+    store_tile(acc, a.dX, a.H, tm * kBM, a.nc, tn * kBN, a.H, a.acc_dx, wave, lane);
   } else {
     KMajorLoader la, lb;
-    la.init(G, ldg, tm * kBM, vc_pad, nc_pad, wave, lane);
-    lb.init(Xc, H, tn * kBN, H, nc, wave, lane);
-    tile_mainloop<true, true>(la, lb, nc_pad, lds, acc);
-    store_tile(acc, dW, H, tm * kBM, vc, tn * kBN, H, acc_dw, wave, lane);
+    la.init(a.G, a.ldg, tm * kBM, a.vc_pad, a.nc_pad, wave, lane);
+    lb.init(a.Xc, a.H, tn * kBN, a.H, a.nc, wave, lane);
+    tile_mainloop<true, true>(la, lb, a.nc_pad, lds, acc);
+    store_tile(acc, a.dW, a.H, tm * kBM, a.vc, tn * kBN, a.H, a.acc_dw, wave, lane);
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void bwd_step_kernel(GradArgs gr, int grad_slots, BwdGArgs bg,
+                                                               int g_tiles) {
+  __shared__ __attribute__((aligned(1024))) char lds_raw[kMainLds];
+  LCE_LDS char* lds = (LCE_LDS char*)lds_raw;
+  const int id = blockIdx.x;
+  if (id < grad_slots) {
+    grad_tile(gr, id, lds);
+  } else if (id - grad_slots < g_tiles) {
+    recompute_g_tile(bg, id - grad_slots, lds, lds_raw);
   }
 }
 
@@ -460,26 +457,28 @@ hipError_t launch_bwd_scale(const int* targets, int N, int ignore_index, const f
   return last();
 }
 
-hipError_t launch_bwd_g(const uint16_t* X, int N, int H, const uint16_t* Ws, int Vs, int v0, int vc, int n0, int nc,
-                        const int* targets, const float* lse, const float* gscale, int ignore_index, int vocab_base,
-                        int V, uint16_t* G, int ldg, int nc_pad, int vc_pad, hipStream_t st) {
-  const int n_tt = nc_pad / kBN, n_tv = vc_pad / kBM;
-  hipLaunchKernelGGL(bwd_g_kernel, dim3(n_tt * n_tv), dim3(kThreads), 0, st, X, N, H, Ws, Vs, v0, vc, n0, nc, targets,
-                     lse, gscale, ignore_index, vocab_base, V, G, ldg, n_tt, n_tv);
-  return last();
-}
-
-hipError_t launch_grad_gemm(const uint16_t* G, int ldg, int nc_pad, int vc_pad, const uint16_t* Wc, int vc,
-                            const uint16_t* Xc, int nc, int H, float* dX, int acc_dx, float* dW, int acc_dw,
-                            hipStream_t st) {
-  const int n_tiles = H / kBN + (H % kBN ? 1 : 0);
-  const int dx_tiles = (nc_pad / kBM) * n_tiles;
-  const int dw_tiles = (vc_pad / kBM) * n_tiles;
-  const int dw_first = nc_pad > vc_pad ? 1 : 0;  // dW tiles have K = nc_pad, dX tiles K = vc_pad
-  const int first = dw_first ? dw_tiles : dx_tiles, second = dw_first ? dx_tiles : dw_tiles;
-  const int first_slots = (first + 7) & ~7;
-  hipLaunchKernelGGL(grad_gemm_kernel, dim3(first_slots + second), dim3(kThreads), 0, st, G, ldg, nc_pad, vc_pad, Wc,
-                     vc, Xc, nc, H, dX, acc_dx, dW, acc_dw, n_tiles, dw_first, first_slots);
+hipError_t launch_bwd_step(const GradArgs* gr, const BwdGArgs* bg, hipStream_t st) {
+  GradArgs g{};
+  BwdGArgs b{};
+  int grad_slots = 0, g_tiles = 0;
+  if (gr) {
+    g = *gr;
+    g.n_tiles = g.H / kBN + (g.H % kBN ? 1 : 0);
+    const int dx_tiles = (g.nc_pad / kBM) * g.n_tiles;
+    const int dw_tiles = (g.vc_pad / kBM) * g.n_tiles;
+    g.dw_first = g.nc_pad > g.vc_pad ? 1 : 0;  // dW tiles have K = nc_pad, dX tiles K = vc_pad
+    const int first = g.dw_first ? dw_tiles : dx_tiles, second = g.dw_first ? dx_tiles : dw_tiles;
+    g.first_slots = (first + 7) & ~7;
+    grad_slots = (g.first_slots + second + 7) & ~7;
+  }
+  if (bg) {
+    b = *bg;
+    b.n_tt = b.nc_pad / kBN;
+    b.n_tv = b.vc_pad / kBM;
+    g_tiles = b.n_tt * b.n_tv;
+  }
+  if (grad_slots + g_tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_step_kernel, dim3(grad_slots + g_tiles), dim3(kThreads), 0, st, g, grad_slots, b, g_tiles);
   return last();
 }
 
