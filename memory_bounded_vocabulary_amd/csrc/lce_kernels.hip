@@ -359,26 +359,91 @@ __device__ __forceinline__ void recompute_g_tile(const BwdGArgs& a, int id, LCE_
   }
 }
 
-__device__ __forceinline__ void store_tile(const Acc& acc, float* __restrict__ C, int ldc, int m0, int m_valid,
-                                           int n0, int n_valid, int accumulate, int wave, int lane) {
+// Stores (accumulate = 0) or adds (accumulate = 1) the fp32 tile into
+// C[m0 + r][n0 + c] for r < m_valid - m0, c < n_valid - n0 (n_valid a multiple
+// of 4). The tile goes through LDS in two halves of 128 rows (the rows of the
+// waves with wm = 0, then wm = 1), so that global memory sees 16-byte accesses
+// along whole rows, and all of a thread's loads of C are issued before the
+// first of them is waited for. LDS row r holds the 256 floats of the row, with
+// the two 128-byte column halves swapped on rows where (r >> 2) is odd, so the
+// two 32-lane halves of an accumulator write (rows r and r + 4) use different
+// banks. Needs the 128 KB of LDS free (the main loop ends on a barrier).
+// kIt 16-byte chunks of one 128-row half, in batches of kBatch: a batch's
+// loads of C are all issued before the first is waited for.
+template <int kIt, bool kFull, bool kAcc>
+__device__ __forceinline__ void rmw_half(float* __restrict__ C, int ldc, int r0, int m_valid, int n0, int n_valid,
+                                         const float* tile) {
+  constexpr int kBatch = 8;
+  const int c = threadIdx.x & 63;
+  const int gc = n0 + 4 * c;
 #pragma unroll
-  for (int i = 0; i < kMI; ++i)
+  for (int b0 = 0; b0 < kIt; b0 += kBatch) {
+    float4 old[kBatch];
+    if (kAcc) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int r = m0 + acc_row(wave, lane, i, e);
-      if (r >= m_valid) continue;
-#pragma unroll
-      for (int j = 0; j < kNI; ++j) {
-        const int c = n0 + acc_col(wave, lane, j);
-        if (c < n_valid) {
-          float* p = C + (size_t)r * ldc + c;
-          *p = accumulate ? *p + acc[i][j][e] : acc[i][j][e];
-        }
+      for (int k = 0; k < kBatch; ++k) {
+        const int r = (b0 + k) * (kThreads / 64) + (threadIdx.x >> 6);
+        const int gr = r0 + r;
+        old[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (kFull || (gr < m_valid && gc < n_valid)) old[k] = *reinterpret_cast<const float4*>(C + (size_t)gr * ldc + gc);
       }
     }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int r = (b0 + k) * (kThreads / 64) + (threadIdx.x >> 6);
+      const int gr = r0 + r;
+      if (kFull || (gr < m_valid && gc < n_valid)) {
+        float4 v = *reinterpret_cast<const float4*>(tile + r * 256 + 4 * (c ^ (8 * ((r >> 2) & 1))));
+        if (kAcc) {
+          v.x += old[k].x;
+          v.y += old[k].y;
+          v.z += old[k].z;
+          v.w += old[k].w;
+        }
+        *reinterpret_cast<float4*>(C + (size_t)gr * ldc + gc) = v;
+      }
+    }
+  }
 }
 
-__device__ __forceinline__ void grad_tile(const GradArgs& a, int id, LCE_LDS char* lds) {
+__device__ __forceinline__ void store_tile(const Acc& acc, float* __restrict__ C, int ldc, int m0, int m_valid,
+                                           int n0, int n_valid, int accumulate, char* ldsg) {
+  const int wave = wave_id();
+  const int lane = lane_id();
+  const int wm = wave / kWN, wn = wave % kWN;
+  const bool full = m0 + kBM <= m_valid && n0 + kBN <= n_valid;
+  float* tile = reinterpret_cast<float*>(ldsg);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (wm == h) {
+#pragma unroll
+      for (int i = 0; i < kMI; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int r = 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+#pragma unroll
+          for (int j = 0; j < kNI; ++j) {
+            const int c = wn * kWaveN + 32 * j + (lane & 31);
+            tile[r * 256 + (c ^ (32 * ((r >> 2) & 1)))] = acc[i][j][e];
+          }
+        }
+    }
+    __syncthreads();
+    constexpr int kIt = 128 * 64 / kThreads;  // 16-byte chunks per thread
+    const int r0 = m0 + 128 * h;
+    if (full && accumulate)
+      rmw_half<kIt, true, true>(C, ldc, r0, m_valid, n0, n_valid, tile);
+    else if (full)
+      rmw_half<kIt, true, false>(C, ldc, r0, m_valid, n0, n_valid, tile);
+    else if (accumulate)
+      rmw_half<kIt, false, true>(C, ldc, r0, m_valid, n0, n_valid, tile);
+    else
+      rmw_half<kIt, false, false>(C, ldc, r0, m_valid, n0, n_valid, tile);
+    __syncthreads();
+  }
+}
+
+__device__ __forceinline__ void grad_tile(const GradArgs& a, int id, LCE_LDS char* lds, char* ldsg) {
   const int wave = wave_id();
   const int lane = lane_id();
   const int dx_rows = a.nc_pad / kBM, dw_rows = a.vc_pad / kBM;
@@ -400,13 +465,13 @@ __device__ __forceinline__ void grad_tile(const GradArgs& a, int id, LCE_LDS cha
     la.init(a.G, a.ldg, tm * kBM, a.nc_pad, wave, lane);
     lb.init(a.Wc, a.H, tn * kBN, a.H, a.vc, wave, lane);
     tile_mainloop<false, true>(la, lb, a.vc_pad, lds, acc);
-    store_tile(acc, a.dX, a.H, tm * kBM, a.nc, tn * kBN, a.H, a.acc_dx, wave, lane);
+    store_tile(acc, a.dX, a.H, tm * kBM, a.nc, tn * kBN, a.H, a.acc_dx, ldsg);
   } else {
     KMajorLoader la, lb;
     la.init(a.G, a.ldg, tm * kBM, a.vc_pad, a.nc_pad, wave, lane);
     lb.init(a.Xc, a.H, tn * kBN, a.H, a.nc, wave, lane);
     tile_mainloop<true, true>(la, lb, a.nc_pad, lds, acc);
-    store_tile(acc, a.dW, a.H, tm * kBM, a.vc, tn * kBN, a.H, a.acc_dw, wave, lane);
+    store_tile(acc, a.dW, a.H, tm * kBM, a.vc, tn * kBN, a.H, a.acc_dw, ldsg);
   }
 }
 
@@ -416,7 +481,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_step_kernel(GradArgs gr, int 
   LCE_LDS char* lds = (LCE_LDS char*)lds_raw;
   const int id = blockIdx.x;
   if (id < grad_slots) {
-    grad_tile(gr, id, lds);
+    grad_tile(gr, id, lds, lds_raw);
   } else if (id - grad_slots < g_tiles) {
     recompute_g_tile(bg, id - grad_slots, lds, lds_raw);
   }
