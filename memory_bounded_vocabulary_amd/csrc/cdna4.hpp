@@ -30,10 +30,23 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// 16-byte global -> LDS copy issued by a whole wave: lane l's 16 bytes land at
-// lds_wave_base + 16*l. lds_wave_base must be wave-uniform.
-__device__ __forceinline__ void g2lds16(const void* gsrc, LCE_LDS void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, lds_wave_base, 16, 0, 0);
+// 16-byte global -> LDS copy issued by a whole wave (direct load into LDS):
+// lane l's 16 bytes, read at base + voff (voff per lane), land at
+// lds_wave_base + 16*l. base and lds_wave_base must be wave-uniform.
+//
+// Issued as inline assembly on purpose: the compiler's wait-count pass
+// otherwise decides, depending on register allocation, that later LDS reads
+// of the *other* buffer must wait for these loads, which serialises the
+// pipeline. The callers order LDS explicitly instead: every stage waits with
+// s_waitcnt vmcnt and a barrier before reading what was loaded, and only loads
+// into a buffer after a barrier that retired all reads of it. The compiler
+// does not count these loads in vmcnt, which only makes its own waits for
+// other loads stricter (loads complete in order), never weaker. The asm sets
+// M0; every direct-to-LDS load of the library goes through here, and no other
+// code of these kernels uses M0.
+__device__ __forceinline__ void g2lds16(const void* base, uint32_t voff, LCE_LDS void* lds_wave_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_wave_base);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff), "s"(base));
 }
 
 // Transposing LDS read (gfx950): see KMajorReader for the lane layout.

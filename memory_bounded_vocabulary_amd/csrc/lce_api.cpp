@@ -4,8 +4,8 @@
 // Schedule (one rank's share of "Flattening Every Memory Peak in Long-Context
 // Mixture-of-Experts Training", section 3.2, Ring-DTP):
 //   forward   target logits; round k = 0..P-1 folds shard order[k] into the
-//             per-token running (m, z); finalize lse = m + log z, the token
-//             losses and the loss.
+//             per-token running (m, z); the last round's last arrivals
+//             finalize lse = m + log z, the token losses and the loss.
 //   backward  g = dloss / n_valid; then for every unit (shard in ring order,
 //             vocabulary chunk, token chunk): recompute the logit block from
 //             lse and form G in bf16, then dX += G W_chunk and dW_chunk +=
@@ -58,7 +58,7 @@ struct Plan {
   int64_t splits, tiles_per_split;
   int64_t vs_pad, vcs, ncs;
   // forward workspace
-  size_t off_state, off_yt, off_part, off_nvalid, fwd_bytes;
+  size_t off_state, off_yt, off_part, off_counters, fwd_bytes;
   // backward workspace
   size_t off_gscale, off_g, g_bytes, bwd_bytes;
   size_t bytes;
@@ -117,8 +117,8 @@ Plan make_plan(const lce_dims* d) {
   o = align256(o + size_t(p.n_pad) * 4);
   p.off_part = o;
   o = align256(o + size_t(p.token_blocks) * 16);
-  p.off_nvalid = o;
-  o = align256(o + 16);
+  p.off_counters = o;
+  o = align256(o + size_t(p.token_blocks + 1) * 4);
   p.fwd_bytes = o;
 
   o = 0;
@@ -172,9 +172,8 @@ int hip_status(hipError_t e, const char* what) {
 }
 
 // ---- optional per-launch event trace (see lce_trace_enable) ----
-enum Kind { kTargetLogit, kFwdRound, kFinalize, kBwdScale, kBwdG, kBwdStep, kGradGemm, kKinds };
-const char* const kKindName[kKinds] = {"target_logit", "fwd_round", "finalize", "bwd_scale", "bwd_g", "bwd_step",
-                                       "grad_gemm"};
+enum Kind { kTargetLogit, kFwdRound, kBwdScale, kBwdG, kBwdStep, kGradGemm, kKinds };
+const char* const kKindName[kKinds] = {"target_logit", "fwd_round", "bwd_scale", "bwd_g", "bwd_step", "grad_gemm"};
 
 struct Trace {
   std::vector<hipEvent_t> ev;  // pairs: [2i] before, [2i+1] after launch i
@@ -231,39 +230,54 @@ int lce_forward(const lce_dims* d, const void* hidden, const void* const* w_shar
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  float2* state = reinterpret_cast<float2*>(ws + p.off_state);
-  float* yt = reinterpret_cast<float*>(ws + p.off_yt);
-  double2* part = reinterpret_cast<double2*>(ws + p.off_part);
-  float* nvalid = reinterpret_cast<float*>(ws + p.off_nvalid);
   const uint16_t* X = static_cast<const uint16_t*>(hidden);
   const int N = int(p.N), H = int(p.H), Vs = int(p.Vs), V = int(p.V);
 
-  lce::ShardTable table{};
-  for (int k = 0; k < d->n_shards; ++k) table.p[k] = static_cast<const uint16_t*>(w_shards[k]);
-  const double dN = double(p.N), dH = double(p.H), dVs = double(p.Vs), dS = double(p.splits);
+  lce::ShardTable by_id{}, by_round{};
+  for (int k = 0; k < d->n_shards; ++k) {
+    by_id.p[k] = static_cast<const uint16_t*>(w_shards[k]);
+    by_round.p[k] = static_cast<const uint16_t*>(w_shards[order[k]]);
+  }
+  lce::FwdArgs a{};
+  a.X = X;
+  a.targets = targets;
+  a.yt = reinterpret_cast<float*>(ws + p.off_yt);
+  a.state = reinterpret_cast<float2*>(ws + p.off_state);
+  a.counters = reinterpret_cast<int*>(ws + p.off_counters);
+  a.partials = reinterpret_cast<double2*>(ws + p.off_part);
+  a.lse = lse;
+  a.token_loss = token_loss;
+  a.loss = loss;
+  a.N = N;
+  a.H = H;
+  a.Vs = Vs;
+  a.P = d->n_shards;
+  a.state_ld = int(p.n_pad);
+  a.token_blocks = int(p.token_blocks);
+  a.S = int(p.splits);
+  a.tiles_per_split = int(p.tiles_per_split);
+  a.n_vtiles = int(p.vocab_tiles);
+  a.ignore_index = d->ignore_index;
+  a.reduction = d->reduction;
+  const double dN = double(p.N), dH = double(p.H), dS = double(p.splits);
   st = hip_status(traced(kTargetLogit, 0.0, 4.0 * dN * dH + 8.0 * dN, s,
-                         [&] { return lce::launch_target_logit(X, N, H, table, Vs, V, targets, d->ignore_index, yt, s); }),
+                         [&] {
+                           return lce::launch_target_logit(X, N, H, by_id, Vs, V, targets, d->ignore_index,
+                                                            const_cast<float*>(a.yt), a.counters,
+                                                            a.token_blocks + 1, s);
+                         }),
                   "target logits");
   if (st) return st;
+  const double dVs = double(p.Vs);
   for (int k = 0; k < d->n_shards; ++k) {
-    const uint16_t* W = static_cast<const uint16_t*>(w_shards[order[k]]);
-    const int first = k == 0;
-    st = hip_status(traced(kFwdRound, 2.0 * dN * dVs * dH, 2.0 * dN * dH + 2.0 * dVs * dH + (first ? 8.0 : 16.0) * dS * dN, s,
-                           [&] {
-                             return lce::launch_fwd_round(X, N, H, W, Vs, state, int(p.n_pad), int(p.token_blocks),
-                                                          int(p.splits), int(p.tiles_per_split), int(p.vocab_tiles),
-                                                          first, s);
-                           }),
+    const int first = k == 0, last = k == d->n_shards - 1;
+    st = hip_status(traced(kFwdRound, 2.0 * dN * dVs * dH,
+                           2.0 * dN * dH + 2.0 * dVs * dH + (first ? 8.0 : 16.0) * dS * dN + (last ? 16.0 * dN : 0.0), s,
+                           [&] { return lce::launch_fwd_round(a, by_round.p[k], first, last, s); }),
                     "forward round");
     if (st) return st;
   }
-  return hip_status(traced(kFinalize, 0.0, 8.0 * dS * dN + 16.0 * dN, s,
-                           [&] {
-                             return lce::launch_finalize(state, int(p.n_pad), int(p.splits), yt, targets, N,
-                                                         d->ignore_index, lse, token_loss, part, d->reduction, loss,
-                                                         nvalid, s);
-                           }),
-                    "finalize");
+  return LCE_OK;
 }
 
 int lce_backward(const lce_dims* d, const void* hidden, const void* const* w_shards, const int32_t* shard_order,

@@ -14,13 +14,23 @@ struct ShardTable {
   const uint16_t* p[kMaxShards];
 };
 
-hipError_t launch_fwd_round(const uint16_t* X, int N, int H, const uint16_t* W, int Vs, float2* state, int state_ld,
-                            int token_blocks, int S, int tiles_per_split, int n_vtiles, int first, hipStream_t st);
+// One forward round; the last round also finalizes.
+struct FwdArgs {
+  const uint16_t* X;        // hidden [N][H]
+  const int* targets;
+  const float* yt;          // target logits from launch_target_logit
+  float2* state;            // [S][state_ld] per-split (m, z), log2 domain
+  int* counters;            // token_blocks + 1 arrival counters, zeroed by launch_target_logit
+  double2* partials;        // [token_blocks] (loss sum, count)
+  float* lse;               // [N]
+  float* token_loss;        // [N] or NULL
+  float* loss;              // scalar
+  int N, H, Vs, P, state_ld, token_blocks, S, tiles_per_split, n_vtiles, ignore_index, reduction;
+};
+hipError_t launch_fwd_round(const FwdArgs& a, const uint16_t* W, int first, int last_round, hipStream_t st);
 hipError_t launch_target_logit(const uint16_t* X, int N, int H, const ShardTable& shards, int Vs, int V,
-                               const int* targets, int ignore_index, float* yt, hipStream_t st);
-hipError_t launch_finalize(const float2* state, int state_ld, int S, const float* yt, const int* targets, int N,
-                           int ignore_index, float* lse, float* token_loss, double2* partials, int reduction,
-                           float* loss, float* n_valid_out, hipStream_t st);
+                               const int* targets, int ignore_index, float* yt, int* counters, int n_counters,
+                               hipStream_t st);
 hipError_t launch_bwd_scale(const int* targets, int N, int ignore_index, const float* dloss, int reduction,
                             float* gscale, hipStream_t st);
 // Recompute + G of one backward unit (shard, vocabulary chunk, token chunk).

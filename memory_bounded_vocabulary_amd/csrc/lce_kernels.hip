@@ -21,15 +21,24 @@ namespace lce {
 // (tokens), so that in the MFMA accumulator layout each lane owns whole token
 // columns: lane l of wave (wm, wn) holds tokens wn*64 + 32 j + l % 32 (j = 0, 1)
 // and, for each, 64 of the tile's 256 vocabulary rows. The online (m, z) of a
-// token therefore lives in two registers per lane and the fold needs no
-// cross-lane traffic until the very end.
+// token (log2 domain) therefore lives in two registers per lane and the fold
+// needs no cross-lane traffic until the end of the round.
 //
-// Grid: token blocks x S splits, in the XCD-grouped order of xcd_tile.
-// Workgroup (tb, s) owns tokens [256 tb, 256 tb + 256) and the vocabulary
-// tiles [s*tps, min((s+1)*tps, n_vtiles)) of the shard. Its (m, z) per token is merged, in a fixed order, into state[s][token]
-// once per round, so over the rounds each split meets the shards in ring
-// order. Every (s, token) has exactly one writer per launch and launches are
-// ordered on the stream: no atomics, bitwise-reproducible.
+// One launch per round (the shard a ring would deliver in that round). Grid:
+// token blocks x S splits, in the XCD-grouped order of xcd_tile. Workgroup
+// (tb, s) owns tokens [256 tb, 256 tb + 256) and the shard's vocabulary tiles
+// [s*tps, min((s+1)*tps, n_vtiles)); while it folds a tile, the first two LDS
+// stages of its next tile are already loading. Its (m, z) per token is merged
+// into state[s][token] after the earlier rounds' (one writer per entry per
+// launch, launches ordered on the stream: no atomics on data).
+//
+// Finalize, fused into the last round: the last of a token block's S
+// workgroups to finish (an atomic arrival counter per block) merges the S
+// states in split order, writes lse = (m + log2 z) ln 2 and the token losses,
+// and a partial sum of the block; the last block to finish sums the partials
+// in block order. All merges run in a fixed order, so the result is bitwise
+// reproducible. The counters are zeroed by target_logit_kernel, which runs
+// first.
 // --------------------------------------------------------------------------
 __device__ __forceinline__ void fold_full(const Acc& acc, float (&m)[kNI], float (&z)[kNI]) {
 #pragma unroll
@@ -50,7 +59,7 @@ __device__ __forceinline__ void fold_full(const Acc& acc, float (&m)[kNI], float
   }
 }
 
-// Same, for the shard's last tile: vocabulary rows at or past `live` (relative
+// Same, for a shard's last tile: vocabulary rows at or past `live` (relative
 // to this lane's first row) act as -infinity.
 __device__ __forceinline__ void fold_masked(const Acc& acc, float (&m)[kNI], float (&z)[kNI], int live) {
 #pragma unroll
@@ -76,51 +85,49 @@ __device__ __forceinline__ void fold_masked(const Acc& acc, float (&m)[kNI], flo
   }
 }
 
-__global__ __launch_bounds__(kThreads, 1) void fwd_round_kernel(const uint16_t* __restrict__ X, int N, int H,
-                                                                const uint16_t* __restrict__ W, int Vs,
-                                                                float2* __restrict__ state, int state_ld,
-                                                                int token_blocks, int S, int tiles_per_split,
-                                                                int n_vtiles, int first) {
-  __shared__ __attribute__((aligned(1024))) char lds_raw[kMainLds];
-  LCE_LDS char* lds = (LCE_LDS char*)lds_raw;
+// Fixed-order tree sum over the first 256 threads of a block (deterministic).
+__device__ __forceinline__ void block_sum256(double& a, long long& b, double* sa, long long* sb) {
+  const int t = threadIdx.x;
+  if (t < 256) {
+    sa[t] = a;
+    sb[t] = b;
+  }
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (t < w) {
+      sa[t] += sa[t + w];
+      sb[t] += sb[t + w];
+    }
+    __syncthreads();
+  }
+  a = sa[0];
+  b = sb[0];
+}
+
+// A workgroup's end: merge the lanes' and waves' (m, z) of its 256 tokens and
+// merge that into state[split][token] (after the earlier rounds'); in the last
+// round, if this is the last of the token block's S splits to arrive, the
+// block's finalize, and if that is the last block, the loss.
+__device__ __forceinline__ void fwd_finish_item(const FwdArgs& a, int tb, int split, const float (&m_in)[kNI],
+                                               const float (&z_in)[kNI], int first, int last, char* lds_raw,
+                                               int* s_last_p) {
+  int& s_last = *s_last_p;
   const int wave = wave_id();
   const int lane = lane_id();
   const int wm = wave / kWN, wn = wave % kWN;
-  int tb, split;
-  xcd_tile(blockIdx.x, token_blocks, S, tb, split);
-  const int t0 = split * tiles_per_split;
-  const int t1 = min(t0 + tiles_per_split, n_vtiles);
-
-  KContigLoader lx;
-  lx.init(X, H, tb * kBN, N, wave, lane);
   float m[kNI], z[kNI];
-#pragma unroll
-  for (int j = 0; j < kNI; ++j) {
-    m[j] = kNegBig;
-    z[j] = 0.0f;
-  }
-  const int lane_row = wm * kWaveM + 4 * (lane >> 5);  // first vocabulary row of this lane in a tile
-  for (int vt = t0; vt < t1; ++vt) {
-    KContigLoader lw;
-    lw.init(W, H, vt * kBM, Vs, wave, lane);
-    Acc acc;
-    tile_mainloop<false, false>(lw, lx, H, lds, acc);
-    const int live = Vs - vt * kBM;
-    if (live >= kBM)
-      fold_full(acc, m, z);
-    else
-      fold_masked(acc, m, z, live - lane_row);
-  }
-
   // lanes l and l ^ 32 hold the same tokens (different vocabulary rows)
 #pragma unroll
   for (int j = 0; j < kNI; ++j) {
+    m[j] = m_in[j];
+    z[j] = z_in[j];
     const float m2 = __shfl_xor(m[j], 32);
     const float z2 = __shfl_xor(z[j], 32);
     lse_merge(m[j], z[j], m2, z2);
   }
   // waves wm = 1 hand their tokens' state to waves wm = 0 (LDS is free: the
-  // main loop ended on a barrier)
+  // main loop ended on a barrier and no load is in flight)
+  __syncthreads();
   float2* red = reinterpret_cast<float2*>(lds_raw);
   if (wm == 1 && lane < 32) {
 #pragma unroll
@@ -134,9 +141,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_round_kernel(const uint16_t* 
       float M = m[j], Z = z[j];
       lse_merge(M, Z, o.x, o.y);
       const int row = tb * kBN + wn * kWaveN + 32 * j + lane;
-      if (row < N) {
-        float2* sp = state + (size_t)split * state_ld + row;
-        if (!first) {
+      if (row < a.N) {
+        float2* sp = a.state + (size_t)split * a.state_ld + row;
+        if (!first) {  // earlier rounds come first in the merge
           const float2 p = *sp;
           float M0 = p.x, Z0 = p.y;
           lse_merge(M0, Z0, M, Z);
@@ -147,17 +154,111 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_round_kernel(const uint16_t* 
       }
     }
   }
+  if (!last) return;
+
+  // ---- fused finalize: the last split of this token block to arrive ----
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = atomicAdd(&a.counters[tb], 1) == a.S - 1;
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  double* sa = reinterpret_cast<double*>(lds_raw + 4096);
+  long long* sb = reinterpret_cast<long long*>(lds_raw + 8192);
+  double l = 0.0;
+  long long cnt = 0;
+  const int row = tb * kBN + threadIdx.x;
+  if (threadIdx.x < 256 && row < a.N) {
+    float M = kNegBig, Z = 0.0f;
+    for (int s = 0; s < a.S; ++s) {
+      const float2 p = a.state[(size_t)s * a.state_ld + row];
+      lse_merge(M, Z, p.x, p.y);
+    }
+    const float lse = (M + fast_log2(Z)) * kLn2;
+    a.lse[row] = lse;
+    float tl = 0.0f;
+    if (a.targets[row] != a.ignore_index) {
+      tl = lse - a.yt[row];
+      cnt = 1;
+    }
+    if (a.token_loss) a.token_loss[row] = tl;
+    l = tl;
+  }
+  block_sum256(l, cnt, sa, sb);
+  if (threadIdx.x == 0) a.partials[tb] = make_double2(l, (double)cnt);
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = atomicAdd(&a.counters[a.token_blocks], 1) == a.token_blocks - 1;
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  // ---- the last token block: the loss, summing the block partials in order ----
+  double s = 0.0;
+  long long c = 0;
+  if (threadIdx.x < 256) {
+    for (int b = threadIdx.x; b < a.token_blocks; b += 256) {
+      const double2 p = a.partials[b];
+      s += p.x;
+      c += (long long)p.y;
+    }
+  }
+  block_sum256(s, c, sa, sb);
+  if (threadIdx.x == 0) a.loss[0] = (float)(a.reduction == 0 ? s / (double)c : s);
+}
+
+__global__ __launch_bounds__(kThreads, 1) void fwd_round_kernel(FwdArgs a, const uint16_t* __restrict__ W,
+                                                                int first, int last) {
+  __shared__ __attribute__((aligned(1024))) char lds_raw[kMainLds];
+  __shared__ int s_last;
+  LCE_LDS char* lds = (LCE_LDS char*)lds_raw;
+  const int wave = wave_id();
+  const int lane = lane_id();
+  const int wm = wave / kWN;
+  int tb, split;
+  xcd_tile(blockIdx.x, a.token_blocks, a.S, tb, split);
+  const int t0 = split * a.tiles_per_split;
+  const int t1 = min(t0 + a.tiles_per_split, a.n_vtiles);
+
+  float m[kNI], z[kNI];
+#pragma unroll
+  for (int j = 0; j < kNI; ++j) {
+    m[j] = kNegBig;
+    z[j] = 0.0f;
+  }
+  const int lane_row = wm * kWaveM + 4 * (lane >> 5);  // first vocabulary row of this lane in a tile
+  KContigLoader lx, lw;
+  lx.init(a.X, a.H, tb * kBN, a.N, wave, lane);
+  lw.init(W, a.H, t0 * kBM, a.Vs, wave, lane);
+  tile_prologue(lw, lx, a.H, lds);
+  for (int vt = t0; vt < t1; ++vt) {
+    Acc acc;
+    tile_mainloop<false, false, true>(lw, lx, a.H, lds, acc);
+    if (vt + 1 < t1) {  // the next tile's first stages load while this one folds
+      lw.init(W, a.H, (vt + 1) * kBM, a.Vs, wave, lane);
+      tile_prologue(lw, lx, a.H, lds);
+    }
+    const int live = a.Vs - vt * kBM;
+    if (live >= kBM)
+      fold_full(acc, m, z);
+    else
+      fold_masked(acc, m, z, live - lane_row);
+  }
+  fwd_finish_item(a, tb, split, m, z, first, last, lds_raw, &s_last);
 }
 
 // --------------------------------------------------------------------------
 // Target logit y_t = x_i . w_{t_i} (fp32 accumulation), one wave per token, read
 // from the shard that owns t_i. Ignored tokens get 0; a target outside [0, V)
-// gets NaN so the token's loss, and the mean, become NaN.
+// gets NaN so the token's loss, and the mean, become NaN. Also zeroes the
+// forward kernel's arrival counters.
 // --------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void target_logit_kernel(const uint16_t* __restrict__ X, int N, int H,
                                                            ShardTable shards, int Vs, int V,
                                                            const int* __restrict__ targets, int ignore_index,
-                                                           float* __restrict__ yt) {
+                                                           float* __restrict__ yt, int* __restrict__ counters,
+                                                           int n_counters) {
+  // zero the forward's arrival counters (this kernel runs first)
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n_counters; i += gridDim.x * 256) counters[i] = 0;
   const int lane = lane_id();
   const int row = blockIdx.x * 4 + wave_id();
   if (row >= N) return;
@@ -200,54 +301,6 @@ __device__ __forceinline__ void block_sum2(double& a, long long& b) {
   }
   a = sa[0];
   b = sb[0];
-}
-
-// --------------------------------------------------------------------------
-// Finalize: merge the S split states in order; lse = (m + log2 z) ln 2; token
-// loss lse - y_t for valid tokens, 0 for ignored ones; per-block partial sums.
-// --------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void finalize_kernel(const float2* __restrict__ state, int state_ld, int S,
-                                                       const float* __restrict__ yt,
-                                                       const int* __restrict__ targets, int N, int ignore_index,
-                                                       float* __restrict__ lse_out,
-                                                       float* __restrict__ token_loss,
-                                                       double2* __restrict__ partials) {
-  const int row = blockIdx.x * 256 + threadIdx.x;
-  double l = 0.0;
-  long long cnt = 0;
-  if (row < N) {
-    float M = kNegBig, Z = 0.0f;
-    for (int s = 0; s < S; ++s) {
-      const float2 p = state[(size_t)s * state_ld + row];
-      lse_merge(M, Z, p.x, p.y);
-    }
-    const float lse = (M + fast_log2(Z)) * kLn2;
-    lse_out[row] = lse;
-    float tl = 0.0f;
-    if (targets[row] != ignore_index) {
-      tl = lse - yt[row];
-      cnt = 1;
-    }
-    if (token_loss) token_loss[row] = tl;
-    l = tl;
-  }
-  block_sum2(l, cnt);
-  if (threadIdx.x == 0) partials[blockIdx.x] = make_double2(l, (double)cnt);
-}
-
-__global__ __launch_bounds__(256) void loss_reduce_kernel(const double2* __restrict__ partials, int n, int reduction,
-                                                          float* __restrict__ loss, float* __restrict__ n_valid_out) {
-  double s = 0.0;
-  long long c = 0;
-  for (int i = threadIdx.x; i < n; i += 256) {
-    s += partials[i].x;
-    c += (long long)partials[i].y;
-  }
-  block_sum2(s, c);
-  if (threadIdx.x == 0) {
-    loss[0] = (float)(reduction == 0 ? s / (double)c : s);
-    if (n_valid_out) n_valid_out[0] = (float)c;
-  }
 }
 
 // --------------------------------------------------------------------------
@@ -490,29 +543,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_step_kernel(GradArgs gr, int 
 // ============================ host launchers ==============================
 static inline hipError_t last() { return hipGetLastError(); }
 
-hipError_t launch_fwd_round(const uint16_t* X, int N, int H, const uint16_t* W, int Vs, float2* state, int state_ld,
-                            int token_blocks, int S, int tiles_per_split, int n_vtiles, int first, hipStream_t st) {
-  hipLaunchKernelGGL(fwd_round_kernel, dim3(token_blocks * S), dim3(kThreads), 0, st, X, N, H, W, Vs, state,
-                     state_ld, token_blocks, S, tiles_per_split, n_vtiles, first);
+hipError_t launch_fwd_round(const FwdArgs& a, const uint16_t* W, int first, int last_round, hipStream_t st) {
+  hipLaunchKernelGGL(fwd_round_kernel, dim3(a.token_blocks * a.S), dim3(kThreads), 0, st, a, W, first, last_round);
   return last();
 }
 
 hipError_t launch_target_logit(const uint16_t* X, int N, int H, const ShardTable& shards, int Vs, int V,
-                               const int* targets, int ignore_index, float* yt, hipStream_t st) {
+                               const int* targets, int ignore_index, float* yt, int* counters, int n_counters,
+                               hipStream_t st) {
   hipLaunchKernelGGL(target_logit_kernel, dim3((N + 3) / 4), dim3(256), 0, st, X, N, H, shards, Vs, V, targets,
-                     ignore_index, yt);
-  return last();
-}
-
-hipError_t launch_finalize(const float2* state, int state_ld, int S, const float* yt, const int* targets, int N,
-                           int ignore_index, float* lse, float* token_loss, double2* partials, int reduction,
-                           float* loss, float* n_valid_out, hipStream_t st) {
-  const int nb = (N + 255) / 256;
-  hipLaunchKernelGGL(finalize_kernel, dim3(nb), dim3(256), 0, st, state, state_ld, S, yt, targets, N, ignore_index,
-                     lse, token_loss, partials);
-  hipError_t e = last();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(loss_reduce_kernel, dim3(1), dim3(256), 0, st, partials, nb, reduction, loss, n_valid_out);
+                     ignore_index, yt, counters, n_counters);
   return last();
 }
 

@@ -75,7 +75,7 @@ struct KContigLoader {
   }
   __device__ __forceinline__ void issue(int k0, LCE_LDS char* tile, int wave) const {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) g2lds16(base + off[j] + (uint32_t)k0 * 2u, tile + (wave * 4 + j) * 1024);
+    for (int j = 0; j < 4; ++j) g2lds16(base, off[j] + (uint32_t)k0 * 2u, tile + (wave * 4 + j) * 1024);
   }
 };
 
@@ -108,7 +108,7 @@ struct KMajorLoader {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t kr = (uint32_t)min(k0 + row[j], k_last);
-      g2lds16(base + kr * ld2 + col[j], tile + (wave * 4 + j) * 1024);
+      g2lds16(base, kr * ld2 + col[j], tile + (wave * 4 + j) * 1024);
     }
   }
 };
@@ -253,11 +253,27 @@ __device__ __forceinline__ void mainloop_stage(int kt, const LA& la, const LB& l
   }
 }
 
+// Issues the loads of the first two stages of a tile (one if K = 64). A caller
+// that has a next tile can issue them as soon as the previous tile_mainloop
+// returned (both LDS stages are then free) and do other work, such as an
+// epilogue, while they fly; it then passes kIssued = true.
+template <class LA, class LB>
+__device__ __forceinline__ void tile_prologue(const LA& la, const LB& lb, int K, LCE_LDS char* lds) {
+  const int wave = wave_id();
+  la.issue(0, lds, wave);
+  lb.issue(0, lds + kOpBytes, wave);
+  if (K > kBK) {
+    la.issue(kBK, lds + kStageBytes, wave);
+    lb.issue(kBK, lds + kStageBytes + kOpBytes, wave);
+  }
+}
+
 // Full K loop for one tile (K a positive multiple of 64). The accumulators are
-// zeroed here. On return every wave has passed a barrier after its last LDS
-// read and no load into LDS is in flight, so both LDS stages are free for the
-// caller.
-template <bool A_KMAJ, bool B_KMAJ, class LA, class LB>
+// zeroed here. With kIssued the first stages were issued by tile_prologue and
+// the wave has issued no other memory operation since. On return every wave
+// has passed a barrier after its last LDS read and no load into LDS is in
+// flight, so both LDS stages are free for the caller.
+template <bool A_KMAJ, bool B_KMAJ, bool kIssued = false, class LA, class LB>
 __device__ __forceinline__ void tile_mainloop(const LA& la, const LB& lb, int K, LCE_LDS char* lds, Acc& acc) {
   const int wave = wave_id();
   const int lane = lane_id();
@@ -271,15 +287,11 @@ __device__ __forceinline__ void tile_mainloop(const LA& la, const LB& lb, int K,
 #pragma unroll
     for (int j = 0; j < kNI; ++j) acc[i][j] = f32x16{};
   const int kt_n = K / kBK;
-  la.issue(0, lds, wave);
-  lb.issue(0, lds + kOpBytes, wave);
-  if (kt_n > 1) {
-    la.issue(kBK, lds + kStageBytes, wave);
-    lb.issue(kBK, lds + kStageBytes + kOpBytes, wave);
+  if (!kIssued) tile_prologue(la, lb, K, lds);
+  if (kt_n > 1)
     wait_vm<8>();  // stage 0 landed (the 8 loads of stage 1 may still fly)
-  } else {
+  else
     wait_vm0();
-  }
   __syncthreads();
   bf16x8 a0[kMI], b0[kNI], a1[kMI], b1[kNI];
   ra.read(lds, 0, lane, a0);
