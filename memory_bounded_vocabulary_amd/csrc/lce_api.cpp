@@ -268,13 +268,17 @@ int lce_forward(const lce_dims* d, const void* hidden, const void* const* w_shar
                          }),
                   "target logits");
   if (st) return st;
+  // All rounds in one launch when every workgroup is resident at once (its
+  // state then stays in registers); else one launch per round.
+  const int P = d->n_shards;
+  const int per_launch = p.token_blocks * p.splits <= kTargetWorkgroups ? P : 1;
   const double dVs = double(p.Vs);
-  for (int k = 0; k < d->n_shards; ++k) {
-    const int first = k == 0, last = k == d->n_shards - 1;
-    st = hip_status(traced(kFwdRound, 2.0 * dN * dVs * dH,
-                           2.0 * dN * dH + 2.0 * dVs * dH + (first ? 8.0 : 16.0) * dS * dN + (last ? 16.0 * dN : 0.0), s,
-                           [&] { return lce::launch_fwd_round(a, by_round.p[k], first, last, s); }),
-                    "forward round");
+  for (int k = 0; k < P; k += per_launch) {
+    const int k1 = std::min(P, k + per_launch), nr = k1 - k;
+    const double flops = 2.0 * dN * dVs * dH * nr;
+    const double bytes = 2.0 * dN * dH + 2.0 * dVs * dH * nr + (k == 0 ? 8.0 : 16.0) * dS * dN + (k1 == P ? 16.0 * dN : 0.0);
+    st = hip_status(traced(kFwdRound, flops, bytes, s, [&] { return lce::launch_fwd_rounds(a, by_round, k, k1, s); }),
+                    "forward rounds");
     if (st) return st;
   }
   return LCE_OK;

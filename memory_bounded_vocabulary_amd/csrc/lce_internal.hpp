@@ -14,7 +14,8 @@ struct ShardTable {
   const uint16_t* p[kMaxShards];
 };
 
-// One forward round; the last round also finalizes.
+// Forward rounds [k_begin, k_end) in one launch; the launch that ends with round
+// P - 1 also finalizes.
 struct FwdArgs {
   const uint16_t* X;        // hidden [N][H]
   const int* targets;
@@ -27,7 +28,8 @@ struct FwdArgs {
   float* loss;              // scalar
   int N, H, Vs, P, state_ld, token_blocks, S, tiles_per_split, n_vtiles, ignore_index, reduction;
 };
-hipError_t launch_fwd_round(const FwdArgs& a, const uint16_t* W, int first, int last_round, hipStream_t st);
+// shards.p[k] is the shard met in round k (the host applies the ring order).
+hipError_t launch_fwd_rounds(const FwdArgs& a, const ShardTable& shards, int k_begin, int k_end, hipStream_t st);
 hipError_t launch_target_logit(const uint16_t* X, int N, int H, const ShardTable& shards, int Vs, int V,
                                const int* targets, int ignore_index, float* yt, int* counters, int n_counters,
                                hipStream_t st);

@@ -24,13 +24,18 @@ namespace lce {
 // token (log2 domain) therefore lives in two registers per lane and the fold
 // needs no cross-lane traffic until the end of the round.
 //
-// One launch per round (the shard a ring would deliver in that round). Grid:
-// token blocks x S splits, in the XCD-grouped order of xcd_tile. Workgroup
-// (tb, s) owns tokens [256 tb, 256 tb + 256) and the shard's vocabulary tiles
-// [s*tps, min((s+1)*tps, n_vtiles)); while it folds a tile, the first two LDS
-// stages of its next tile are already loading. Its (m, z) per token is merged
-// into state[s][token] after the earlier rounds' (one writer per entry per
-// launch, launches ordered on the stream: no atomics on data).
+// A launch covers rounds [k_begin, k_end) (round k meets shards.p[k], the
+// shard a ring would deliver then; the host permutes the table into ring
+// order). Grid: token blocks x S splits, in the XCD-grouped order of xcd_tile.
+// Workgroup (tb, s) owns tokens [256 tb, 256 tb + 256) and, in each of its
+// rounds, the shard's vocabulary tiles [s*tps, min((s+1)*tps, n_vtiles)),
+// keeping (m, z) in registers across them; while it folds a tile, the first
+// two LDS stages of its next tile are already loading. At the end its (m, z)
+// per token is merged into state[s][token] after the earlier launches' (one
+// writer per entry per launch, launches ordered on the stream: no atomics on
+// data). When the grid fits on the CUs at once, one launch covers all rounds;
+// otherwise one launch per round keeps every CU on the same shard, which then
+// stays in the caches.
 //
 // Finalize, fused into the last round: the last of a token block's S
 // workgroups to finish (an atomic arrival counter per block) merges the S
@@ -206,8 +211,8 @@ __device__ __forceinline__ void fwd_finish_item(const FwdArgs& a, int tb, int sp
   if (threadIdx.x == 0) a.loss[0] = (float)(a.reduction == 0 ? s / (double)c : s);
 }
 
-__global__ __launch_bounds__(kThreads, 1) void fwd_round_kernel(FwdArgs a, const uint16_t* __restrict__ W,
-                                                                int first, int last) {
+__global__ __launch_bounds__(kThreads, 1) void fwd_round_kernel(FwdArgs a, ShardTable shards, int k_begin,
+                                                                int k_end) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[kMainLds];
   __shared__ int s_last;
   LCE_LDS char* lds = (LCE_LDS char*)lds_raw;
@@ -217,7 +222,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_round_kernel(FwdArgs a, const
   int tb, split;
   xcd_tile(blockIdx.x, a.token_blocks, a.S, tb, split);
   const int t0 = split * a.tiles_per_split;
-  const int t1 = min(t0 + a.tiles_per_split, a.n_vtiles);
+  const int n_my = min(t0 + a.tiles_per_split, a.n_vtiles) - t0;  // tiles per shard
+  const int n_all = (k_end - k_begin) * n_my;
 
   float m[kNI], z[kNI];
 #pragma unroll
@@ -228,13 +234,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_round_kernel(FwdArgs a, const
   const int lane_row = wm * kWaveM + 4 * (lane >> 5);  // first vocabulary row of this lane in a tile
   KContigLoader lx, lw;
   lx.init(a.X, a.H, tb * kBN, a.N, wave, lane);
-  lw.init(W, a.H, t0 * kBM, a.Vs, wave, lane);
+  lw.init(shards.p[k_begin], a.H, t0 * kBM, a.Vs, wave, lane);
   tile_prologue(lw, lx, a.H, lds);
-  for (int vt = t0; vt < t1; ++vt) {
+  for (int i = 0; i < n_all; ++i) {
+    const int vt = t0 + i % n_my;
     Acc acc;
     tile_mainloop<false, false, true>(lw, lx, a.H, lds, acc);
-    if (vt + 1 < t1) {  // the next tile's first stages load while this one folds
-      lw.init(W, a.H, (vt + 1) * kBM, a.Vs, wave, lane);
+    if (i + 1 < n_all) {  // the next tile's first stages load while this one folds
+      lw.init(shards.p[k_begin + (i + 1) / n_my], a.H, (t0 + (i + 1) % n_my) * kBM, a.Vs, wave, lane);
       tile_prologue(lw, lx, a.H, lds);
     }
     const int live = a.Vs - vt * kBM;
@@ -243,7 +250,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_round_kernel(FwdArgs a, const
     else
       fold_masked(acc, m, z, live - lane_row);
   }
-  fwd_finish_item(a, tb, split, m, z, first, last, lds_raw, &s_last);
+  fwd_finish_item(a, tb, split, m, z, k_begin == 0, k_end == a.P, lds_raw, &s_last);
 }
 
 // --------------------------------------------------------------------------
@@ -543,8 +550,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_step_kernel(GradArgs gr, int 
 // ============================ host launchers ==============================
 static inline hipError_t last() { return hipGetLastError(); }
 
-hipError_t launch_fwd_round(const FwdArgs& a, const uint16_t* W, int first, int last_round, hipStream_t st) {
-  hipLaunchKernelGGL(fwd_round_kernel, dim3(a.token_blocks * a.S), dim3(kThreads), 0, st, a, W, first, last_round);
+hipError_t launch_fwd_rounds(const FwdArgs& a, const ShardTable& shards, int k_begin, int k_end, hipStream_t st) {
+  hipLaunchKernelGGL(fwd_round_kernel, dim3(a.token_blocks * a.S), dim3(kThreads), 0, st, a, shards, k_begin, k_end);
   return last();
 }
 
