@@ -68,16 +68,23 @@ def cpu_baseline(batch, target_s: float):
     x_all = batch.hidden
     wt = oracle.bf16_to_f64(batch.weight)
 
-    def run(n):
+    def run(n, reps=1):
         x = oracle.bf16_to_f64(x_all[:n])
         t0 = time.perf_counter()
-        oracle.cross_entropy(x, wt, batch.targets[:n])
+        for _ in range(reps):
+            oracle.cross_entropy(x, wt, batch.targets[:n])
         return time.perf_counter() - t0
 
+    # calibrate on a few tokens, then take a prefix of the batch sized for
+    # about target_s seconds; if the whole batch takes less, repeat it
     n_cal = max(8, min(w.n_tokens, int(2e10 / (6.0 * w.hidden * w.vocab))))
     t_cal = run(n_cal)
     n = int(min(w.n_tokens, max(n_cal, n_cal * target_s / max(t_cal, 1e-3))))
     t = run(n) if n != n_cal else t_cal
+    reps = 1
+    if n == w.n_tokens and t < 0.66 * target_s:
+        reps = max(1, int(target_s / max(t, 1e-3)))
+        t = run(n, reps)
     cpu = "unknown"
     try:
         for line in open("/proc/cpuinfo"):
@@ -87,9 +94,10 @@ def cpu_baseline(batch, target_s: float):
     except OSError:
         pass
     del np
-    return {"value": n / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"first {n} of {w.n_tokens} tokens of the {w.name} batch at full H={w.hidden}, "
-                      f"V={w.vocab}, P={w.n_shards}; float64 numpy/BLAS, forward+backward, {t:.1f} s",
+    what = f"first {n} of {w.n_tokens} tokens" if n < w.n_tokens else f"all {n} tokens ({reps} passes)"
+    return {"value": n * reps / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{what} of the {w.name} batch at full H={w.hidden}, V={w.vocab}, P={w.n_shards}; "
+                      f"float64 numpy/BLAS, forward+backward, {t:.1f} s",
             "blas": blas, "cpu": cpu, "affinity_cores": len(os.sched_getaffinity(0))}
 
 

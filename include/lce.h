@@ -69,9 +69,9 @@ typedef struct lce_dims {
 
 /*
  * Bytes of device workspace lce_forward and lce_backward need for `dims`.
- * Pure host function. The size grows with N and H and is bounded independently
- * of V: it holds per-token state (O(N)), a transposed copy of the hidden states
- * (N*H bf16) and fixed-size gradient chunks, never a logit strip.
+ * Pure host function. The size is bounded independently of V: it holds
+ * per-token state (O(N)) and two gradient chunks of at most 16384 x 8192 bf16
+ * (fixed-size, whatever N and V), never a logit strip.
  * Returns 0 if dims is invalid.
  */
 LCE_API size_t lce_workspace_bytes(const lce_dims* dims);
