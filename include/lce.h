@@ -118,6 +118,61 @@ LCE_API int lce_backward(const lce_dims* dims, const void* hidden, const void* c
                  float* const* d_w_shards, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * One ring round at a time (same page, section 3.2 and Fig. 3: in each of
+ * the P rounds a rank computes against the shard it currently holds, then
+ * passes it on; backward makes the same trip). A ring driver holding one
+ * shard at a time calls these in place of lce_forward / lce_backward, moving
+ * the shards between rounds itself:
+ *
+ *   for k in 0..P-1: lce_fwd_round(dims, k, id_k, hidden, shard_k, targets, ws)
+ *   lce_fwd_finish(dims, targets, loss, lse, token_loss, ws)
+ *   for k in 0..P-1: lce_bwd_round(dims, k, id_k, hidden, shard_k, targets,
+ *                                  lse, dloss, d_hidden, d_shard_k, acc, ws)
+ *
+ * id_k is the shard id (0..P-1) of the shard held in round k; the ids of the
+ * P rounds must be a permutation of 0..P-1. The per-token running state
+ * (m, z) and the target logits stay in `workspace` between the calls of one
+ * forward, so every call of a sequence gets the same workspace (at least
+ * lce_workspace_bytes(dims) bytes) and nothing else may use it meanwhile; the
+ * stream order between the calls is the caller's to keep (one stream, or
+ * events). Results match lce_forward / lce_backward with shard_order[k] = id_k:
+ * the backward bit for bit, the forward up to fp32 rounding (its running state
+ * is merged once per round here, possibly once per call there).
+ *
+ * lce_fwd_round
+ *  round        k, 0..P-1. Round 0 starts a new forward (resets the state).
+ *  shard_index  the id of the shard passed in w_shard.
+ *  hidden, targets  as for lce_forward; w_shard device bf16 [V/P][H].
+ *  Folds the logits of every token against this shard into the state and
+ *  fills the target logits that fall in this shard.
+ *
+ * lce_fwd_finish
+ *  After the P rounds: writes loss, lse and (if non-NULL) token_loss exactly
+ *  as lce_forward does. Calling it before all P rounds have run gives the
+ *  loss of the shards seen so far, with NaN token losses for targets in the
+ *  missing shards.
+ *
+ * lce_bwd_round
+ *  round, shard_index, hidden, w_shard, targets  as for lce_fwd_round.
+ *  lse, dloss   as for lce_backward (round 0 reads dloss; the scale it
+ *               derives is kept in the workspace for the later rounds).
+ *  d_hidden     device fp32 [N][H]: round 0 overwrites it, later rounds add
+ *               this shard's part, so after round P-1 it holds dL/dX.
+ *  d_w_shard    device fp32 [V/P][H]: this shard's gradient, overwritten, or
+ *               added to what it holds when accumulate_dw != 0 (a driver that
+ *               sums a travelling partial, or accumulates over micro-batches).
+ * The forward's workspace contents are not needed by the backward rounds;
+ * lce_fwd_round must not run between backward rounds on the same workspace.
+ */
+LCE_API int lce_fwd_round(const lce_dims* dims, int round, int shard_index, const void* hidden, const void* w_shard,
+                          const int32_t* targets, void* workspace, size_t workspace_bytes, void* stream);
+LCE_API int lce_fwd_finish(const lce_dims* dims, const int32_t* targets, float* loss, float* lse, float* token_loss,
+                           void* workspace, size_t workspace_bytes, void* stream);
+LCE_API int lce_bwd_round(const lce_dims* dims, int round, int shard_index, const void* hidden, const void* w_shard,
+                          const int32_t* targets, const float* lse, const float* dloss, float* d_hidden,
+                          float* d_w_shard, int accumulate_dw, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Kernel timing trace, for measurement (off by default).
  * lce_trace_enable(capacity) creates `capacity` pairs of HIP events for the
  * calling thread (capacity 0 disables the trace and frees them). While enabled,

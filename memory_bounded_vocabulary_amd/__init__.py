@@ -23,8 +23,9 @@ LIB_PATH = os.path.join(HERE, "liblce.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 REDUCTIONS = {"mean": 0, "sum": 1}
-EXPORTED = ("lce_workspace_bytes", "lce_forward", "lce_backward", "lce_trace_enable", "lce_trace_collect",
-            "lce_status_string", "lce_last_error", "lce_version")
+EXPORTED = ("lce_workspace_bytes", "lce_forward", "lce_backward", "lce_fwd_round", "lce_fwd_finish",
+            "lce_bwd_round", "lce_trace_enable", "lce_trace_collect", "lce_status_string", "lce_last_error",
+            "lce_version")
 
 
 class Dims(ctypes.Structure):
@@ -65,6 +66,13 @@ def lib() -> ctypes.CDLL:
     L.lce_backward.argtypes = [dimp, vp, ctypes.POINTER(vp), i32p, vp, vp, vp, vp, ctypes.POINTER(vp), vp,
                                ctypes.c_size_t, vp]
     L.lce_backward.restype = ctypes.c_int
+    ci, sz = ctypes.c_int, ctypes.c_size_t
+    L.lce_fwd_round.argtypes = [dimp, ci, ci, vp, vp, vp, vp, sz, vp]
+    L.lce_fwd_round.restype = ctypes.c_int
+    L.lce_fwd_finish.argtypes = [dimp, vp, vp, vp, vp, vp, sz, vp]
+    L.lce_fwd_finish.restype = ctypes.c_int
+    L.lce_bwd_round.argtypes = [dimp, ci, ci, vp, vp, vp, vp, vp, vp, vp, ci, vp, sz, vp]
+    L.lce_bwd_round.restype = ctypes.c_int
     L.lce_trace_enable.argtypes = [ctypes.c_int]
     L.lce_trace_enable.restype = ctypes.c_int
     L.lce_trace_collect.argtypes = [ctypes.POINTER(TraceEntry), ctypes.c_int]
@@ -172,6 +180,42 @@ def backward(hidden, shards: Sequence, targets, lse, dloss, ignore_index: int = 
                             workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st)
     return d_hidden, d_shards
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def fwd_round(dims: Dims, round_: int, shard_index: int, hidden, shard, targets, workspace, stream=None) -> None:
+    """One forward ring round: fold `shard` (id `shard_index`) into the state held in `workspace`."""
+    _require_cuda(hidden, shard, targets, workspace)
+    _check(lib().lce_fwd_round(ctypes.byref(dims), int(round_), int(shard_index), hidden.data_ptr(),
+                               shard.data_ptr(), targets.data_ptr(), workspace.data_ptr(), _nbytes(workspace),
+                               _stream(stream)))
+
+
+def fwd_finish(dims: Dims, targets, workspace, token_loss: bool = False, stream=None):
+    """After the rounds: (loss, lse) or (loss, lse, token_loss) from the state in `workspace`."""
+    import torch
+    _require_cuda(targets, workspace)
+    n = int(dims.n_tokens)
+    loss = torch.empty((), dtype=torch.float32, device=targets.device)
+    lse = torch.empty(n, dtype=torch.float32, device=targets.device)
+    tl = torch.empty(n, dtype=torch.float32, device=targets.device) if token_loss else None
+    _check(lib().lce_fwd_finish(ctypes.byref(dims), targets.data_ptr(), loss.data_ptr(), lse.data_ptr(),
+                                tl.data_ptr() if tl is not None else None, workspace.data_ptr(),
+                                _nbytes(workspace), _stream(stream)))
+    return (loss, lse, tl) if token_loss else (loss, lse)
+
+
+def bwd_round(dims: Dims, round_: int, shard_index: int, hidden, shard, targets, lse, dloss, d_hidden, d_shard,
+              accumulate_dw: bool, workspace, stream=None) -> None:
+    """One backward ring round: d_hidden (+)= G W_shard, d_shard (+)= G^T X for this shard."""
+    _require_cuda(hidden, shard, targets, lse, dloss, d_hidden, d_shard, workspace)
+    _check(lib().lce_bwd_round(ctypes.byref(dims), int(round_), int(shard_index), hidden.data_ptr(),
+                               shard.data_ptr(), targets.data_ptr(), lse.data_ptr(), dloss.data_ptr(),
+                               d_hidden.data_ptr(), d_shard.data_ptr(), int(bool(accumulate_dw)),
+                               workspace.data_ptr(), _nbytes(workspace), _stream(stream)))
 
 
 def trace_enable(capacity: int) -> None:

@@ -172,8 +172,9 @@ int hip_status(hipError_t e, const char* what) {
 }
 
 // ---- optional per-launch event trace (see lce_trace_enable) ----
-enum Kind { kTargetLogit, kFwdRound, kBwdScale, kBwdG, kBwdStep, kGradGemm, kKinds };
-const char* const kKindName[kKinds] = {"target_logit", "fwd_round", "bwd_scale", "bwd_g", "bwd_step", "grad_gemm"};
+enum Kind { kTargetLogit, kFwdRound, kFinalize, kBwdScale, kBwdG, kBwdStep, kGradGemm, kKinds };
+const char* const kKindName[kKinds] = {"target_logit", "fwd_round", "finalize", "bwd_scale", "bwd_g", "bwd_step",
+                                       "grad_gemm"};
 
 struct Trace {
   std::vector<hipEvent_t> ev;  // pairs: [2i] before, [2i+1] after launch i
@@ -205,6 +206,179 @@ hipError_t traced(Kind kind, double flops, double bytes, hipStream_t s, F&& laun
   return hipSuccess;
 }
 
+// ---- shared pieces of the schedule ----------------------------------------
+
+lce::FwdArgs fwd_args(const Plan& p, const lce_dims* d, const void* hidden, const int32_t* targets, char* ws,
+                      float* loss, float* lse, float* token_loss) {
+  lce::FwdArgs a{};
+  a.X = static_cast<const uint16_t*>(hidden);
+  a.targets = targets;
+  a.yt = reinterpret_cast<float*>(ws + p.off_yt);
+  a.state = reinterpret_cast<float2*>(ws + p.off_state);
+  a.counters = reinterpret_cast<int*>(ws + p.off_counters);
+  a.partials = reinterpret_cast<double2*>(ws + p.off_part);
+  a.lse = lse;
+  a.token_loss = token_loss;
+  a.loss = loss;
+  a.N = int(p.N);
+  a.H = int(p.H);
+  a.Vs = int(p.Vs);
+  a.P = int(p.P);
+  a.state_ld = int(p.n_pad);
+  a.token_blocks = int(p.token_blocks);
+  a.S = int(p.splits);
+  a.tiles_per_split = int(p.tiles_per_split);
+  a.n_vtiles = int(p.vocab_tiles);
+  a.ignore_index = d->ignore_index;
+  a.reduction = d->reduction;
+  return a;
+}
+
+int run_target_logit(const Plan& p, const lce::FwdArgs& a, const lce::ShardTable& by_id, int s_lo, int s_hi, int init,
+                     hipStream_t s) {
+  const double dN = double(p.N), dH = double(p.H);
+  return hip_status(traced(kTargetLogit, 0.0, 4.0 * dN * dH + 8.0 * dN, s,
+                           [&] {
+                             return lce::launch_target_logit(a.X, a.N, a.H, by_id, a.Vs, int(p.V), s_lo, s_hi,
+                                                             a.targets, a.ignore_index, const_cast<float*>(a.yt), init,
+                                                             a.counters, a.token_blocks + 1, s);
+                           }),
+                    "target logits");
+}
+
+int run_fwd_rounds(const Plan& p, const lce::FwdArgs& a, const lce::ShardTable& by_round, int k0, int k1, int first,
+                   int finalize, hipStream_t s) {
+  const double dN = double(p.N), dH = double(p.H), dS = double(p.splits), dVs = double(p.Vs);
+  const int nr = k1 - k0;
+  const double flops = 2.0 * dN * dVs * dH * nr;
+  const double bytes = 2.0 * dN * dH + 2.0 * dVs * dH * nr + (first ? 8.0 : 16.0) * dS * dN + (finalize ? 16.0 * dN : 0.0);
+  return hip_status(
+      traced(kFwdRound, flops, bytes, s, [&] { return lce::launch_fwd_rounds(a, by_round, k0, k1, first, finalize, s); }),
+      "forward rounds");
+}
+
+// One backward unit: a (vocabulary chunk, token chunk) block of one shard.
+struct Unit {
+  int sh, v0, vc, vc_pad, n0, nc, nc_pad;
+  const uint16_t* W;  // the shard
+  float* dW;          // its gradient
+  int acc_dx, acc_dw;
+};
+
+// The units of one shard, in order; acc_dx/acc_dw set from `dx_written`
+// (per token chunk: has dX been written yet in this backward) and `acc_dw`.
+void shard_units(const Plan& p, int sh, const uint16_t* W, float* dW, std::vector<bool>& dx_written, bool acc_dw,
+                 std::vector<Unit>& out) {
+  for (int64_t v0 = 0; v0 < p.Vs; v0 += p.vcs) {
+    const int vc = int(std::min<int64_t>(p.vcs, p.Vs - v0));
+    for (int64_t n0 = 0; n0 < p.N; n0 += p.ncs) {
+      const int nc = int(std::min<int64_t>(p.ncs, p.N - n0));
+      const size_t nchunk = size_t(n0 / p.ncs);
+      Unit u{sh, int(v0), vc, int(round_up(vc, kTile)), int(n0), nc, int(round_up(nc, kTile)), W, dW, 0, 0};
+      u.acc_dx = dx_written[nchunk] ? 1 : 0;
+      dx_written[nchunk] = true;
+      u.acc_dw = (acc_dw || n0 > 0) ? 1 : 0;
+      out.push_back(u);
+    }
+  }
+}
+
+int run_bwd_scale(const Plan& p, const lce_dims* d, const int32_t* targets, const float* dloss, float* gscale,
+                  hipStream_t s) {
+  return hip_status(traced(kBwdScale, 0.0, 4.0 * double(p.N), s,
+                           [&] {
+                             return lce::launch_bwd_scale(targets, int(p.N), d->ignore_index, dloss, d->reduction,
+                                                          gscale, s);
+                           }),
+                    "scale");
+}
+
+// Launch j runs the gradient GEMMs of unit j - 1 and the recompute of unit j.
+int run_bwd_units(const Plan& p, const lce_dims* d, const std::vector<Unit>& units, const uint16_t* X,
+                  const int32_t* targets, const float* lse, const float* gscale, float* d_hidden, char* ws,
+                  hipStream_t s) {
+  const double dH = double(p.H);
+  auto gbuf = [&](size_t u) { return reinterpret_cast<uint16_t*>(ws + p.off_g + (u & 1) * p.g_bytes); };
+  for (size_t j = 0; j <= units.size(); ++j) {
+    lce::GradArgs ga{};
+    lce::BwdGArgs ba{};
+    double flops = 0.0, bytes = 0.0;
+    if (j > 0) {
+      const Unit& u = units[j - 1];
+      ga.G = gbuf(j - 1);
+      ga.ldg = u.vc_pad;
+      ga.nc_pad = u.nc_pad;
+      ga.vc_pad = u.vc_pad;
+      ga.Wc = u.W + size_t(u.v0) * p.H;
+      ga.vc = u.vc;
+      ga.Xc = X + size_t(u.n0) * p.H;
+      ga.nc = u.nc;
+      ga.H = int(p.H);
+      ga.dX = d_hidden + size_t(u.n0) * p.H;
+      ga.acc_dx = u.acc_dx;
+      ga.dW = u.dW + size_t(u.v0) * p.H;
+      ga.acc_dw = u.acc_dw;
+      const double dnc = u.nc, dvc = u.vc, gb = 2.0 * double(u.nc_pad) * double(u.vc_pad);
+      flops += 4.0 * dnc * dvc * dH;
+      bytes += 2.0 * gb + 2.0 * dvc * dH + 2.0 * dnc * dH + (4.0 + 4.0 * u.acc_dx) * dnc * dH +
+               (4.0 + 4.0 * u.acc_dw) * dvc * dH;
+    }
+    if (j < units.size()) {
+      const Unit& u = units[j];
+      ba.X = X;
+      ba.Ws = u.W;
+      ba.targets = targets;
+      ba.lse = lse;
+      ba.gscale = gscale;
+      ba.G = gbuf(j);
+      ba.N = int(p.N);
+      ba.H = int(p.H);
+      ba.Vs = int(p.Vs);
+      ba.v0 = u.v0;
+      ba.vc = u.vc;
+      ba.n0 = u.n0;
+      ba.nc = u.nc;
+      ba.nc_pad = u.nc_pad;
+      ba.vc_pad = u.vc_pad;
+      ba.ignore_index = d->ignore_index;
+      ba.vocab_base = int(u.sh * p.Vs + u.v0);
+      ba.V = int(p.V);
+      ba.ldg = u.vc_pad;
+      const double dnc = u.nc, dvc = u.vc;
+      flops += 2.0 * dnc * dvc * dH;
+      bytes += 2.0 * dnc * dH + 2.0 * dvc * dH + 2.0 * double(u.nc_pad) * double(u.vc_pad) + 12.0 * dnc;
+    }
+    const Kind kind = j == 0 ? kBwdG : (j == units.size() ? kGradGemm : kBwdStep);
+    int st = hip_status(traced(kind, flops, bytes, s,
+                               [&] {
+                                 return lce::launch_bwd_step(j > 0 ? &ga : nullptr, j < units.size() ? &ba : nullptr,
+                                                             s);
+                               }),
+                        "backward step");
+    if (st) return st;
+  }
+  return LCE_OK;
+}
+
+int check_round_args(const lce_dims* d, int round, int shard_index, const void* hidden, const void* w_shard,
+                     const int32_t* targets, void* workspace, size_t workspace_bytes, Plan* plan) {
+  int st = check_dims(d);
+  if (st) return st;
+  if (round < 0 || round >= d->n_shards)
+    return fail(LCE_ERR_INVALID_ARG, "round must be in [0, %d) (got %d)", d->n_shards, round);
+  if (shard_index < 0 || shard_index >= d->n_shards)
+    return fail(LCE_ERR_INVALID_ARG, "shard_index must be in [0, %d) (got %d)", d->n_shards, shard_index);
+  if (!hidden || !w_shard || !targets) return fail(LCE_ERR_INVALID_ARG, "hidden, w_shard and targets must be non-NULL");
+  if (!aligned16(w_shard) || !aligned16(hidden) || !aligned16(targets))
+    return fail(LCE_ERR_UNSUPPORTED, "hidden/w_shard/targets not 16-byte aligned");
+  *plan = make_plan(d);
+  if (!workspace) return fail(LCE_ERR_INVALID_ARG, "workspace is NULL");
+  if (!aligned16(workspace)) return fail(LCE_ERR_UNSUPPORTED, "workspace is not 16-byte aligned");
+  if (workspace_bytes < plan->bytes)
+    return fail(LCE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, plan->bytes);
+  return LCE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -230,55 +404,21 @@ int lce_forward(const lce_dims* d, const void* hidden, const void* const* w_shar
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  const uint16_t* X = static_cast<const uint16_t*>(hidden);
-  const int N = int(p.N), H = int(p.H), Vs = int(p.Vs), V = int(p.V);
-
   lce::ShardTable by_id{}, by_round{};
   for (int k = 0; k < d->n_shards; ++k) {
     by_id.p[k] = static_cast<const uint16_t*>(w_shards[k]);
     by_round.p[k] = static_cast<const uint16_t*>(w_shards[order[k]]);
   }
-  lce::FwdArgs a{};
-  a.X = X;
-  a.targets = targets;
-  a.yt = reinterpret_cast<float*>(ws + p.off_yt);
-  a.state = reinterpret_cast<float2*>(ws + p.off_state);
-  a.counters = reinterpret_cast<int*>(ws + p.off_counters);
-  a.partials = reinterpret_cast<double2*>(ws + p.off_part);
-  a.lse = lse;
-  a.token_loss = token_loss;
-  a.loss = loss;
-  a.N = N;
-  a.H = H;
-  a.Vs = Vs;
-  a.P = d->n_shards;
-  a.state_ld = int(p.n_pad);
-  a.token_blocks = int(p.token_blocks);
-  a.S = int(p.splits);
-  a.tiles_per_split = int(p.tiles_per_split);
-  a.n_vtiles = int(p.vocab_tiles);
-  a.ignore_index = d->ignore_index;
-  a.reduction = d->reduction;
-  const double dN = double(p.N), dH = double(p.H), dS = double(p.splits);
-  st = hip_status(traced(kTargetLogit, 0.0, 4.0 * dN * dH + 8.0 * dN, s,
-                         [&] {
-                           return lce::launch_target_logit(X, N, H, by_id, Vs, V, targets, d->ignore_index,
-                                                            const_cast<float*>(a.yt), a.counters,
-                                                            a.token_blocks + 1, s);
-                         }),
-                  "target logits");
+  const lce::FwdArgs a = fwd_args(p, d, hidden, targets, ws, loss, lse, token_loss);
+  st = run_target_logit(p, a, by_id, 0, d->n_shards, 1, s);
   if (st) return st;
   // All rounds in one launch when every workgroup is resident at once (its
   // state then stays in registers); else one launch per round.
   const int P = d->n_shards;
   const int per_launch = p.token_blocks * p.splits <= kTargetWorkgroups ? P : 1;
-  const double dVs = double(p.Vs);
   for (int k = 0; k < P; k += per_launch) {
-    const int k1 = std::min(P, k + per_launch), nr = k1 - k;
-    const double flops = 2.0 * dN * dVs * dH * nr;
-    const double bytes = 2.0 * dN * dH + 2.0 * dVs * dH * nr + (k == 0 ? 8.0 : 16.0) * dS * dN + (k1 == P ? 16.0 * dN : 0.0);
-    st = hip_status(traced(kFwdRound, flops, bytes, s, [&] { return lce::launch_fwd_rounds(a, by_round, k, k1, s); }),
-                    "forward rounds");
+    const int k1 = std::min(P, k + per_launch);
+    st = run_fwd_rounds(p, a, by_round, k, k1, k == 0, k1 == P, s);
     if (st) return st;
   }
   return LCE_OK;
@@ -305,88 +445,73 @@ int lce_backward(const lce_dims* d, const void* hidden, const void* const* w_sha
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   float* gscale = reinterpret_cast<float*>(ws + p.off_gscale);
-  const uint16_t* X = static_cast<const uint16_t*>(hidden);
-  const int N = int(p.N), H = int(p.H), Vs = int(p.Vs), V = int(p.V);
-
-  const double dN = double(p.N), dH = double(p.H);
-  st = hip_status(traced(kBwdScale, 0.0, 4.0 * dN, s,
-                         [&] { return lce::launch_bwd_scale(targets, N, d->ignore_index, dloss, d->reduction, gscale, s); }),
-                  "scale");
+  st = run_bwd_scale(p, d, targets, dloss, gscale, s);
   if (st) return st;
-  // Backward units in ring order: (shard, vocabulary chunk, token chunk).
-  // Launch j runs the gradient GEMMs of unit j - 1 and the recompute of unit j.
-  struct Unit {
-    int sh, v0, vc, vc_pad, n0, nc, nc_pad;
-  };
   std::vector<Unit> units;
-  for (int k = 0; k < d->n_shards; ++k)
-    for (int64_t v0 = 0; v0 < p.Vs; v0 += p.vcs) {
-      const int vc = int(std::min<int64_t>(p.vcs, p.Vs - v0));
-      for (int64_t n0 = 0; n0 < p.N; n0 += p.ncs) {
-        const int nc = int(std::min<int64_t>(p.ncs, p.N - n0));
-        units.push_back({order[k], int(v0), vc, int(round_up(vc, kTile)), int(n0), nc, int(round_up(nc, kTile))});
-      }
-    }
-  auto gbuf = [&](size_t u) { return reinterpret_cast<uint16_t*>(ws + p.off_g + (u & 1) * p.g_bytes); };
   std::vector<bool> dx_written(size_t(ceil_div(p.N, p.ncs)), false);
-  for (size_t j = 0; j <= units.size(); ++j) {
-    lce::GradArgs ga{};
-    lce::BwdGArgs ba{};
-    double flops = 0.0, bytes = 0.0;
-    if (j > 0) {
-      const Unit& u = units[j - 1];
-      const size_t nchunk = size_t(u.n0 / p.ncs);
-      ga.G = gbuf(j - 1);
-      ga.ldg = u.vc_pad;
-      ga.nc_pad = u.nc_pad;
-      ga.vc_pad = u.vc_pad;
-      ga.Wc = static_cast<const uint16_t*>(w_shards[u.sh]) + size_t(u.v0) * p.H;
-      ga.vc = u.vc;
-      ga.Xc = X + size_t(u.n0) * p.H;
-      ga.nc = u.nc;
-      ga.H = H;
-      ga.dX = d_hidden + size_t(u.n0) * p.H;
-      ga.acc_dx = dx_written[nchunk] ? 1 : 0;
-      dx_written[nchunk] = true;
-      ga.dW = d_w_shards[u.sh] + size_t(u.v0) * p.H;
-      ga.acc_dw = u.n0 > 0 ? 1 : 0;
-      const double dnc = u.nc, dvc = u.vc, gb = 2.0 * double(u.nc_pad) * double(u.vc_pad);
-      flops += 4.0 * dnc * dvc * dH;
-      bytes += 2.0 * gb + 2.0 * dvc * dH + 2.0 * dnc * dH + (4.0 + 4.0 * ga.acc_dx) * dnc * dH +
-               (4.0 + 4.0 * ga.acc_dw) * dvc * dH;
-    }
-    if (j < units.size()) {
-      const Unit& u = units[j];
-      ba.X = X;
-      ba.Ws = static_cast<const uint16_t*>(w_shards[u.sh]);
-      ba.targets = targets;
-      ba.lse = lse;
-      ba.gscale = gscale;
-      ba.G = gbuf(j);
-      ba.N = N;
-      ba.H = H;
-      ba.Vs = Vs;
-      ba.v0 = u.v0;
-      ba.vc = u.vc;
-      ba.n0 = u.n0;
-      ba.nc = u.nc;
-      ba.nc_pad = u.nc_pad;
-      ba.vc_pad = u.vc_pad;
-      ba.ignore_index = d->ignore_index;
-      ba.vocab_base = int(u.sh * p.Vs + u.v0);
-      ba.V = V;
-      ba.ldg = u.vc_pad;
-      const double dnc = u.nc, dvc = u.vc;
-      flops += 2.0 * dnc * dvc * dH;
-      bytes += 2.0 * dnc * dH + 2.0 * dvc * dH + 2.0 * double(u.nc_pad) * double(u.vc_pad) + 12.0 * dnc;
-    }
-    const Kind kind = j == 0 ? kBwdG : (j == units.size() ? kGradGemm : kBwdStep);
-    st = hip_status(traced(kind, flops, bytes, s,
-                           [&] { return lce::launch_bwd_step(j > 0 ? &ga : nullptr, j < units.size() ? &ba : nullptr, s); }),
-                    "backward step");
+  for (int k = 0; k < d->n_shards; ++k)
+    shard_units(p, order[k], static_cast<const uint16_t*>(w_shards[order[k]]), d_w_shards[order[k]], dx_written, false,
+                units);
+  return run_bwd_units(p, d, units, static_cast<const uint16_t*>(hidden), targets, lse, gscale, d_hidden, ws, s);
+}
+
+int lce_fwd_round(const lce_dims* d, int round, int shard_index, const void* hidden, const void* w_shard,
+                  const int32_t* targets, void* workspace, size_t workspace_bytes, void* stream) {
+  Plan p;
+  int st = check_round_args(d, round, shard_index, hidden, w_shard, targets, workspace, workspace_bytes, &p);
+  if (st) return st;
+  g_last_error.clear();
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  lce::ShardTable by_id{}, by_round{};
+  by_id.p[shard_index] = static_cast<const uint16_t*>(w_shard);
+  by_round.p[0] = static_cast<const uint16_t*>(w_shard);
+  const lce::FwdArgs a = fwd_args(p, d, hidden, targets, ws, nullptr, nullptr, nullptr);
+  st = run_target_logit(p, a, by_id, shard_index, shard_index + 1, round == 0, s);
+  if (st) return st;
+  return run_fwd_rounds(p, a, by_round, 0, 1, round == 0, 0, s);
+}
+
+int lce_fwd_finish(const lce_dims* d, const int32_t* targets, float* loss, float* lse, float* token_loss,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_dims(d);
+  if (st) return st;
+  if (!targets || !loss || !lse || !workspace)
+    return fail(LCE_ERR_INVALID_ARG, "targets, loss, lse and workspace must be non-NULL");
+  if (!aligned16(targets) || !aligned16(lse) || (token_loss && !aligned16(token_loss)) || !aligned16(workspace))
+    return fail(LCE_ERR_UNSUPPORTED, "targets/lse/token_loss/workspace not 16-byte aligned");
+  const Plan p = make_plan(d);
+  if (workspace_bytes < p.bytes) return fail(LCE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, p.bytes);
+  g_last_error.clear();
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const lce::FwdArgs a = fwd_args(p, d, nullptr, targets, static_cast<char*>(workspace), loss, lse, token_loss);
+  return hip_status(traced(kFinalize, 0.0, 8.0 * double(p.splits) * double(p.N) + 16.0 * double(p.N), s,
+                           [&] { return lce::launch_finalize(a, s); }),
+                    "finalize");
+}
+
+int lce_bwd_round(const lce_dims* d, int round, int shard_index, const void* hidden, const void* w_shard,
+                  const int32_t* targets, const float* lse, const float* dloss, float* d_hidden, float* d_w_shard,
+                  int accumulate_dw, void* workspace, size_t workspace_bytes, void* stream) {
+  Plan p;
+  int st = check_round_args(d, round, shard_index, hidden, w_shard, targets, workspace, workspace_bytes, &p);
+  if (st) return st;
+  if (!lse || !dloss || !d_hidden || !d_w_shard)
+    return fail(LCE_ERR_INVALID_ARG, "lse, dloss, d_hidden and d_w_shard must be non-NULL");
+  if (!aligned16(lse) || !aligned16(d_hidden) || !aligned16(d_w_shard))
+    return fail(LCE_ERR_UNSUPPORTED, "lse/d_hidden/d_w_shard not 16-byte aligned");
+  g_last_error.clear();
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* gscale = reinterpret_cast<float*>(ws + p.off_gscale);
+  if (round == 0) {
+    st = run_bwd_scale(p, d, targets, dloss, gscale, s);
     if (st) return st;
   }
-  return LCE_OK;
+  std::vector<Unit> units;
+  std::vector<bool> dx_written(size_t(ceil_div(p.N, p.ncs)), round > 0);
+  shard_units(p, shard_index, static_cast<const uint16_t*>(w_shard), d_w_shard, dx_written, accumulate_dw != 0, units);
+  return run_bwd_units(p, d, units, static_cast<const uint16_t*>(hidden), targets, lse, gscale, d_hidden, ws, s);
 }
 
 int lce_trace_enable(int capacity) {
@@ -455,6 +580,6 @@ const char* lce_status_string(int status) {
 
 const char* lce_last_error(void) { return g_last_error.c_str(); }
 
-int lce_version(void) { return (1 << 16) | 0; }
+int lce_version(void) { return (1 << 16) | 1; }
 
 }  // extern "C"

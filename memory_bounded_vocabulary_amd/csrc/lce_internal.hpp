@@ -14,8 +14,9 @@ struct ShardTable {
   const uint16_t* p[kMaxShards];
 };
 
-// Forward rounds [k_begin, k_end) in one launch; the launch that ends with round
-// P - 1 also finalizes.
+// Forward rounds [k_begin, k_end) in one launch (shards.p[k] is the shard met in
+// round k). `first`: no earlier state to merge with. `finalize`: this launch
+// also finalizes (needs target logits of every token already in yt).
 struct FwdArgs {
   const uint16_t* X;        // hidden [N][H]
   const int* targets;
@@ -28,11 +29,15 @@ struct FwdArgs {
   float* loss;              // scalar
   int N, H, Vs, P, state_ld, token_blocks, S, tiles_per_split, n_vtiles, ignore_index, reduction;
 };
-// shards.p[k] is the shard met in round k (the host applies the ring order).
-hipError_t launch_fwd_rounds(const FwdArgs& a, const ShardTable& shards, int k_begin, int k_end, hipStream_t st);
-hipError_t launch_target_logit(const uint16_t* X, int N, int H, const ShardTable& shards, int Vs, int V,
-                               const int* targets, int ignore_index, float* yt, int* counters, int n_counters,
-                               hipStream_t st);
+hipError_t launch_fwd_rounds(const FwdArgs& a, const ShardTable& shards, int k_begin, int k_end, int first,
+                             int finalize, hipStream_t st);
+// Finalize after rounds run one call at a time.
+hipError_t launch_finalize(const FwdArgs& a, hipStream_t st);
+// Target logits of the tokens whose target lies in shards [s_lo, s_hi)
+// (shards.p indexed by shard id); `init` also resets yt and the counters.
+hipError_t launch_target_logit(const uint16_t* X, int N, int H, const ShardTable& shards, int Vs, int V, int s_lo,
+                               int s_hi, const int* targets, int ignore_index, float* yt, int init, int* counters,
+                               int n_counters, hipStream_t st);
 hipError_t launch_bwd_scale(const int* targets, int N, int ignore_index, const float* dloss, int reduction,
                             float* gscale, hipStream_t st);
 // Recompute + G of one backward unit (shard, vocabulary chunk, token chunk).

@@ -212,7 +212,7 @@ __device__ __forceinline__ void fwd_finish_item(const FwdArgs& a, int tb, int sp
 }
 
 __global__ __launch_bounds__(kThreads, 1) void fwd_round_kernel(FwdArgs a, ShardTable shards, int k_begin,
-                                                                int k_end) {
+                                                                int k_end, int first, int finalize) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[kMainLds];
   __shared__ int s_last;
   LCE_LDS char* lds = (LCE_LDS char*)lds_raw;
@@ -250,31 +250,39 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_round_kernel(FwdArgs a, Shard
     else
       fold_masked(acc, m, z, live - lane_row);
   }
-  fwd_finish_item(a, tb, split, m, z, k_begin == 0, k_end == a.P, lds_raw, &s_last);
+  fwd_finish_item(a, tb, split, m, z, first, finalize, lds_raw, &s_last);
 }
 
 // --------------------------------------------------------------------------
 // Target logit y_t = x_i . w_{t_i} (fp32 accumulation), one wave per token, read
-// from the shard that owns t_i. Ignored tokens get 0; a target outside [0, V)
-// gets NaN so the token's loss, and the mean, become NaN. Also zeroes the
-// forward kernel's arrival counters.
+// from the shard that owns t_i, for the tokens whose target lies in the shards
+// [s_lo, s_hi) given (shards.p indexed by shard id). With init, first every
+// ignored token gets 0 and every other token NaN (filled in by this or a later
+// call once its shard is present), and the forward's arrival counters are
+// zeroed: a target outside [0, V) is never filled, so its token's loss, and the
+// mean, stay NaN.
 // --------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void target_logit_kernel(const uint16_t* __restrict__ X, int N, int H,
-                                                           ShardTable shards, int Vs, int V,
+                                                           ShardTable shards, int Vs, int V, int s_lo, int s_hi,
                                                            const int* __restrict__ targets, int ignore_index,
-                                                           float* __restrict__ yt, int* __restrict__ counters,
-                                                           int n_counters) {
-  // zero the forward's arrival counters (this kernel runs first)
-  for (int i = blockIdx.x * 256 + threadIdx.x; i < n_counters; i += gridDim.x * 256) counters[i] = 0;
+                                                           float* __restrict__ yt, int init,
+                                                           int* __restrict__ counters, int n_counters) {
+  if (init) {  // zero the arrival counters of this forward
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n_counters; i += gridDim.x * 256) counters[i] = 0;
+  }
   const int lane = lane_id();
   const int row = blockIdx.x * 4 + wave_id();
   if (row >= N) return;
   const int t = __builtin_amdgcn_readfirstlane(targets[row]);
   if (t == ignore_index || t < 0 || t >= V) {
-    if (lane == 0) yt[row] = (t == ignore_index) ? 0.0f : __builtin_nanf("");
+    if (init && lane == 0) yt[row] = (t == ignore_index) ? 0.0f : __builtin_nanf("");
     return;
   }
   const int s = t / Vs;
+  if (s < s_lo || s >= s_hi) {  // the target's shard is not among these
+    if (init && lane == 0) yt[row] = __builtin_nanf("");
+    return;
+  }
   const uint16_t* w = shards.p[s] + (size_t)(t - s * Vs) * H;
   const uint16_t* x = X + (size_t)row * H;
   float acc = 0.0f;
@@ -547,19 +555,76 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_step_kernel(GradArgs gr, int 
   }
 }
 
+// --------------------------------------------------------------------------
+// Standalone finalize (after rounds run one call at a time): block tb merges
+// the S split states of its 256 tokens in split order, writes lse and the
+// token losses and a partial sum; the last block to finish (arrival counter
+// zeroed by the first round's target_logit_kernel) sums the partials in block
+// order into the loss.
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void finalize_kernel(FwdArgs a) {
+  __shared__ double sa[256];
+  __shared__ long long sb[256];
+  __shared__ int s_last;
+  const int tb = blockIdx.x;
+  const int row = tb * 256 + threadIdx.x;
+  double l = 0.0;
+  long long cnt = 0;
+  if (row < a.N) {
+    float M = kNegBig, Z = 0.0f;
+    for (int s = 0; s < a.S; ++s) {
+      const float2 p = a.state[(size_t)s * a.state_ld + row];
+      lse_merge(M, Z, p.x, p.y);
+    }
+    const float lse = (M + fast_log2(Z)) * kLn2;
+    a.lse[row] = lse;
+    float tl = 0.0f;
+    if (a.targets[row] != a.ignore_index) {
+      tl = lse - a.yt[row];
+      cnt = 1;
+    }
+    if (a.token_loss) a.token_loss[row] = tl;
+    l = tl;
+  }
+  block_sum256(l, cnt, sa, sb);
+  if (threadIdx.x == 0) a.partials[tb] = make_double2(l, (double)cnt);
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = atomicAdd(&a.counters[a.token_blocks], 1) == a.token_blocks - 1;
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  double s = 0.0;
+  long long c = 0;
+  for (int b = threadIdx.x; b < a.token_blocks; b += 256) {
+    const double2 p = a.partials[b];
+    s += p.x;
+    c += (long long)p.y;
+  }
+  block_sum256(s, c, sa, sb);
+  if (threadIdx.x == 0) a.loss[0] = (float)(a.reduction == 0 ? s / (double)c : s);
+}
+
 // ============================ host launchers ==============================
 static inline hipError_t last() { return hipGetLastError(); }
 
-hipError_t launch_fwd_rounds(const FwdArgs& a, const ShardTable& shards, int k_begin, int k_end, hipStream_t st) {
-  hipLaunchKernelGGL(fwd_round_kernel, dim3(a.token_blocks * a.S), dim3(kThreads), 0, st, a, shards, k_begin, k_end);
+hipError_t launch_fwd_rounds(const FwdArgs& a, const ShardTable& shards, int k_begin, int k_end, int first,
+                             int finalize, hipStream_t st) {
+  hipLaunchKernelGGL(fwd_round_kernel, dim3(a.token_blocks * a.S), dim3(kThreads), 0, st, a, shards, k_begin, k_end,
+                     first, finalize);
   return last();
 }
 
-hipError_t launch_target_logit(const uint16_t* X, int N, int H, const ShardTable& shards, int Vs, int V,
-                               const int* targets, int ignore_index, float* yt, int* counters, int n_counters,
-                               hipStream_t st) {
-  hipLaunchKernelGGL(target_logit_kernel, dim3((N + 3) / 4), dim3(256), 0, st, X, N, H, shards, Vs, V, targets,
-                     ignore_index, yt, counters, n_counters);
+hipError_t launch_finalize(const FwdArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(finalize_kernel, dim3(a.token_blocks), dim3(256), 0, st, a);
+  return last();
+}
+
+hipError_t launch_target_logit(const uint16_t* X, int N, int H, const ShardTable& shards, int Vs, int V, int s_lo,
+                               int s_hi, const int* targets, int ignore_index, float* yt, int init, int* counters,
+                               int n_counters, hipStream_t st) {
+  hipLaunchKernelGGL(target_logit_kernel, dim3((N + 3) / 4), dim3(256), 0, st, X, N, H, shards, Vs, V, s_lo, s_hi,
+                     targets, ignore_index, yt, init, counters, n_counters);
   return last();
 }
 

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     L = lce.lib()
     for name in declared_symbols():
         assert hasattr(L, name), name
-    assert lce.version() == (1, 0)
+    assert lce.version() == (1, 1)
 
 
 def test_single_hip_runtime_in_process():
@@ -138,3 +138,49 @@ def test_workspace_is_bounded_independently_of_vocab():
     assert bound < strip_bytes
     # and it is O(N): doubling V at fixed N never grows it past the bound
     assert lce.workspace_bytes(n, h, 8 * 128256 * 2, 8) <= bound
+
+
+def _fwd_round(d, rnd=0, shard=0, hidden=FAKE, w=FAKE, targets=FAKE, ws=FAKE, ws_bytes=None):
+    L = lce.lib()
+    if ws_bytes is None:
+        ws_bytes = L.lce_workspace_bytes(ctypes.byref(d))
+    return L.lce_fwd_round(ctypes.byref(d), rnd, shard, hidden, w, targets, ws, ws_bytes, None)
+
+
+def _fwd_finish(d, targets=FAKE, loss=FAKE, lse=FAKE, tl=None, ws=FAKE, ws_bytes=None):
+    L = lce.lib()
+    if ws_bytes is None:
+        ws_bytes = L.lce_workspace_bytes(ctypes.byref(d))
+    return L.lce_fwd_finish(ctypes.byref(d), targets, loss, lse, tl, ws, ws_bytes, None)
+
+
+def _bwd_round(d, rnd=0, shard=0, w=FAKE, lse=FAKE, dloss=FAKE, dx=FAKE, dw=FAKE, ws=FAKE, ws_bytes=None):
+    L = lce.lib()
+    if ws_bytes is None:
+        ws_bytes = L.lce_workspace_bytes(ctypes.byref(d))
+    return L.lce_bwd_round(ctypes.byref(d), rnd, shard, FAKE, w, FAKE, lse, dloss, dx, dw, 0, ws, ws_bytes, None)
+
+
+def test_round_entry_points_reject_bad_arguments():
+    d = _dims()
+    for bad in (-1, 4):
+        assert _fwd_round(d, rnd=bad) == lce.ERR_INVALID_ARG
+        assert "round" in lce.lib().lce_last_error().decode()
+        assert _fwd_round(d, shard=bad) == lce.ERR_INVALID_ARG
+        assert _bwd_round(d, rnd=bad) == lce.ERR_INVALID_ARG
+        assert _bwd_round(d, shard=bad) == lce.ERR_INVALID_ARG
+    assert _fwd_round(d, w=None) == lce.ERR_INVALID_ARG
+    assert _fwd_round(d, hidden=None) == lce.ERR_INVALID_ARG
+    assert _fwd_round(d, w=FAKE + 8) == lce.ERR_UNSUPPORTED
+    assert _fwd_round(d, ws=None) == lce.ERR_INVALID_ARG
+    assert _fwd_round(_dims(h=100)) == lce.ERR_UNSUPPORTED
+    assert _fwd_finish(d, loss=None) == lce.ERR_INVALID_ARG
+    assert _fwd_finish(d, lse=FAKE + 4) == lce.ERR_UNSUPPORTED
+    assert _fwd_finish(d, tl=FAKE + 4) == lce.ERR_UNSUPPORTED
+    assert _bwd_round(d, dw=None) == lce.ERR_INVALID_ARG
+    assert _bwd_round(d, dloss=None) == lce.ERR_INVALID_ARG
+    assert _bwd_round(d, dw=FAKE + 4) == lce.ERR_UNSUPPORTED
+    need = lce.lib().lce_workspace_bytes(ctypes.byref(d))
+    assert _fwd_round(d, ws_bytes=need - 1) == lce.ERR_WORKSPACE
+    assert _fwd_finish(d, ws_bytes=need - 1) == lce.ERR_WORKSPACE
+    assert _bwd_round(d, ws_bytes=need - 1) == lce.ERR_WORKSPACE

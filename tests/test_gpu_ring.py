@@ -1,0 +1,158 @@
+"""GPU parity of the one-round-at-a-time entry points, driven as a simulated
+ring on one GPU.
+
+P virtual ranks each hold a distinct batch (hidden, targets) and share one
+vocabulary weight cut into P shards. In round k rank r holds shard
+(r - k) mod P, the shard its left neighbour held in round k - 1, so each shard
+visits every rank once ("Flattening Every Memory Peak in Long-Context
+Mixture-of-Experts Training", section 3.2 and Fig. 3). Backward makes the same
+trip, and each shard's gradient travels with the shard: a rank adds its part
+to the partial it receives (accumulate_dw from round 1 on), so after P rounds
+the shard's gradient holds the sum over all ranks' batches.
+
+Each rank is checked against the oracle's ring fold of its own batch in its own
+shard order; the shard gradients against the sum of the ranks' oracle
+gradients.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_support import GRAD_TOL, LOSS_TOL, compare, rel_max, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+BASE = workloads.WORKLOADS["tiny"]
+
+RINGS = [
+    # name, N per rank, H, V, P
+    ("4 ranks, ragged shard", 600, 256, 4 * 300, 4),
+    ("2 ranks, two vocab chunks", 300, 64, 2 * 9000, 2),
+    ("3 ranks, ragged N", 257, 192, 3 * 256, 3),
+    ("8 ranks", 512, 128, 8 * 512, 8),
+]
+
+
+def _ring(name, n, h, v, p, seed0=20):
+    import torch
+    import memory_bounded_vocabulary_amd as lce
+    w = BASE.with_dims(name=name, n_tokens=n, hidden=h, vocab=v, n_shards=p, ignore_frac=0.1, w_std=0.05)
+    weight = workloads.make(w, seed=seed0).weight
+    batches = [workloads.make(w, seed=seed0 + 1 + r, weight=weight) for r in range(p)]
+    dev = [to_device(b) for b in batches]
+    shards = dev[0][1]  # the weight is the same for every rank
+    dims = lce.make_dims(n, h, v, p)
+    ws = [lce.alloc_workspace(n, h, v, p) for _ in range(p)]
+    for k in range(p):
+        for r in range(p):
+            s = (r - k) % p
+            lce.fwd_round(dims, k, s, dev[r][0], shards[s], dev[r][2], ws[r])
+    outs = [lce.fwd_finish(dims, dev[r][2], ws[r], token_loss=True) for r in range(p)]
+    dloss = torch.ones((), dtype=torch.float32, device="cuda")
+    dx = [torch.empty((n, h), dtype=torch.float32, device="cuda") for _ in range(p)]
+    dws = [torch.empty((v // p, h), dtype=torch.float32, device="cuda") for _ in range(p)]
+    for k in range(p):
+        for r in range(p):
+            s = (r - k) % p
+            lce.bwd_round(dims, k, s, dev[r][0], shards[s], dev[r][2], outs[r][1], dloss, dx[r], dws[s], k > 0, ws[r])
+    torch.cuda.synchronize()
+    return batches, dev, outs, dx, dws
+
+
+@pytest.mark.parametrize("case", RINGS, ids=[c[0] for c in RINGS])
+def test_ring_simulation_parity(case):
+    name, n, h, v, p = case
+    say("ring", name, dict(N=n, H=h, V=v, P=p))
+    batches, dev, outs, dx, dws = _ring(name, n, h, v, p)
+    vs = v // p
+    w64 = oracle.bf16_to_f64(batches[0].weight)
+    w_shards = [w64[s * vs:(s + 1) * vs] for s in range(p)]
+    dw_sum = np.zeros_like(w64)
+    for r, b in enumerate(batches):
+        order = [(r - k) % p for k in range(p)]
+        ref = oracle.ring_fold(oracle.bf16_to_f64(b.hidden), w_shards, order, b.targets)
+        dw_sum += ref.d_weight
+        loss, lse, tl = outs[r]
+        got = {
+            "loss": float(loss.item()),
+            "lse": lse.cpu().numpy().astype(np.float64),
+            "token_loss": tl.cpu().numpy().astype(np.float64),
+            "d_hidden": dx[r].cpu().numpy().astype(np.float64),
+            "d_weight": ref.d_weight,  # compared summed over ranks below
+        }
+        compare(got, ref, f"{name} rank {r}")
+        ign = b.targets == -100
+        assert np.all(got["token_loss"][ign] == 0.0) and np.all(got["d_hidden"][ign] == 0.0)
+    got_dw = np.concatenate([d.cpu().numpy() for d in dws]).astype(np.float64)
+    e = rel_max(got_dw, dw_sum)
+    say(f"{name}: summed dW rel={e:.2e}")
+    assert e <= GRAD_TOL
+
+
+def test_rounds_match_whole_pass():
+    """Per-round calls against lce_forward / lce_backward with the same shard
+    order: the backward bit for bit (the same launches on the same data), the
+    forward within the loss tolerance (the running state is merged once per
+    round instead of once per call)."""
+    import torch
+    import memory_bounded_vocabulary_amd as lce
+    w = BASE.with_dims(name="rounds vs whole", n_tokens=700, hidden=256, vocab=4 * 1000, n_shards=4,
+                       ignore_frac=0.1, w_std=0.05)
+    b = workloads.make(w, seed=5)
+    hidden, shards, targets = to_device(b)
+    order = [2, 0, 3, 1]
+    say("rounds vs whole pass", order)
+    loss, lse, tl = lce.forward(hidden, shards, targets, order=order, token_loss=True)
+    dx, dws = lce.backward(hidden, shards, targets, lse, 1.0, order=order)
+    dims = lce.make_dims(w.n_tokens, w.hidden, w.vocab, w.n_shards)
+    ws = lce.alloc_workspace(w.n_tokens, w.hidden, w.vocab, w.n_shards)
+    for k, s in enumerate(order):
+        lce.fwd_round(dims, k, s, hidden, shards[s], targets, ws)
+    loss_r, lse_r, tl_r = lce.fwd_finish(dims, targets, ws, token_loss=True)
+    dloss = torch.ones((), dtype=torch.float32, device="cuda")
+    dx_r = torch.empty_like(dx)
+    dws_r = [torch.empty_like(d) for d in dws]
+    for k, s in enumerate(order):
+        lce.bwd_round(dims, k, s, hidden, shards[s], targets, lse, dloss, dx_r, dws_r[s], False, ws)
+    torch.cuda.synchronize()
+    assert abs(loss_r.item() - loss.item()) <= LOSS_TOL
+    assert float((lse_r - lse).abs().max().item()) <= LOSS_TOL
+    assert float((tl_r - tl).abs().max().item()) <= LOSS_TOL
+    assert torch.equal(dx_r, dx)
+    for a, c in zip(dws_r, dws):
+        assert torch.equal(a, c)
+
+
+def test_accumulate_into_existing_gradient():
+    """accumulate_dw adds the shard gradient to what the buffer holds (gradient
+    accumulation over micro-batches): two micro-batches accumulated into a
+    buffer with prior content equal the prior content plus both gradients."""
+    import torch
+    import memory_bounded_vocabulary_amd as lce
+    w = BASE.with_dims(name="accumulate", n_tokens=300, hidden=128, vocab=2 * 700, n_shards=2, ignore_frac=0.1,
+                       w_std=0.05)
+    weight = workloads.make(w, seed=7).weight
+    mbs = [workloads.make(w, seed=8 + i, weight=weight) for i in range(2)]
+    say("accumulate over micro-batches")
+    dims = lce.make_dims(w.n_tokens, w.hidden, w.vocab, w.n_shards)
+    ws = lce.alloc_workspace(w.n_tokens, w.hidden, w.vocab, w.n_shards)
+    rng = np.random.default_rng(1)
+    prior = [rng.standard_normal((w.shard_rows, w.hidden)).astype(np.float32) * 1e-3 for _ in range(2)]
+    dws = [torch.from_numpy(pr.copy()).cuda() for pr in prior]
+    dloss = torch.ones((), dtype=torch.float32, device="cuda")
+    expect = np.concatenate(prior).astype(np.float64)
+    for mb in mbs:
+        hidden, shards, targets = to_device(mb)
+        for k in range(2):
+            lce.fwd_round(dims, k, k, hidden, shards[k], targets, ws)
+        _, lse = lce.fwd_finish(dims, targets, ws)
+        dx = torch.empty((w.n_tokens, w.hidden), dtype=torch.float32, device="cuda")
+        for k in range(2):
+            lce.bwd_round(dims, k, k, hidden, shards[k], targets, lse, dloss, dx, dws[k], True, ws)
+        expect += oracle.cross_entropy(oracle.bf16_to_f64(mb.hidden), oracle.bf16_to_f64(weight), mb.targets).d_weight
+    torch.cuda.synchronize()
+    got = np.concatenate([d.cpu().numpy() for d in dws]).astype(np.float64)
+    e = rel_max(got, expect)
+    say(f"accumulate: rel={e:.2e}")
+    assert e <= GRAD_TOL
