@@ -29,9 +29,12 @@ Readings where the pages are silent (each also listed in the design notes):
 * Eq. 3 (missing) is read as the standard update m' = max(m, max_j y_j),
   z' = z e^(m - m') + sum_j e^(y_j - m').
 * Reduction is the mean over non-ignored tokens (sum optional); ignored tokens
-  (target == ignore_index) have zero loss and zero gradient rows.
+  (target == ignore_index) have zero loss and zero gradient rows. "none"
+  keeps the per-token losses: the objective is sum_i u_i loss_i for a given
+  per-token upstream gradient u (``dloss`` an array), and ``loss`` reports the
+  plain sum.
 * Gradients: G = g_i (softmax_i - onehot(t_i)) with g_i = dloss / n_valid for
-  valid rows (dloss for "sum"), 0 for ignored rows; dX = G W, dW = G^T X, where
+  valid rows (dloss for "sum", dloss[i] for "none"), 0 for ignored rows; dX = G W, dW = G^T X, where
   W is the V x H (vocabulary-major) weight, i.e. the transpose of the pages'
   H x V W_voc.
 * n_valid = 0 under "mean" gives loss NaN (0/0) and all-zero gradients.
@@ -79,15 +82,19 @@ def _prepare(x, t, ignore_index, vocab, dloss, reduction):
         scale = dloss / n_valid if n_valid else 0.0
     elif reduction == "sum":
         scale = dloss
+    elif reduction == "none":
+        scale = np.asarray(dloss, dtype=np.float64)
+        if scale.shape != t.shape:
+            raise ValueError("reduction 'none' takes one dloss per token")
     else:
-        raise ValueError(f"reduction must be 'mean' or 'sum', got {reduction!r}")
+        raise ValueError(f"reduction must be 'mean', 'sum' or 'none', got {reduction!r}")
     g = np.where(valid, scale, 0.0)
     return t, valid, n_valid, g
 
 
 def _reduce(token_loss, n_valid, reduction):
     loss_sum = math.fsum(token_loss.tolist())
-    if reduction == "sum":
+    if reduction in ("sum", "none"):
         return loss_sum, loss_sum
     return (loss_sum / n_valid if n_valid else float("nan")), loss_sum
 

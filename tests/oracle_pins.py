@@ -10,7 +10,9 @@ What each check pins, and where the fact comes from:
   on tiny random instances, without the max shift the oracle uses.
 * torch_reference: torch's float64 cross_entropy + autograd on the CPU.
 * finite_differences: central differences of the mean loss in every entry of
-  X and W; independent of any gradient formula.
+  X and W; independent of any gradient formula. The per-token reduction is
+  pinned the same way, on the objective sum_i u_i loss_i for a random u, and
+  against torch's reduction="none" backward with upstream gradient u.
 * zero_weight: W = 0 makes every logit 0, so each valid token's loss is ln V,
   dX = 0, and dW_v = g (sum of valid x_i / V - sum of valid x_i with t_i = v).
 * logistic: V = 2 reduces to the logistic loss log(1 + exp(y_other - y_t)).
@@ -119,6 +121,41 @@ def check_finite_differences(orc, seed=7):
         assert err <= 1e-6, err
 
 
+def check_per_token_reduction(orc, seed=8):
+    """reduction 'none': gradients of sum_i u_i loss_i, by finite differences of
+    the token losses and by torch's backward of the unreduced loss."""
+    import torch
+    rng = np.random.default_rng(seed)
+    x, w, t = rand_instance(rng, 6, 3, 7, ignore=2)
+    u = rng.standard_normal(6)
+    r = orc.cross_entropy(x, w, t, reduction="none", dloss=u)
+
+    def objective(xx, ww):
+        return float(np.dot(u, orc.cross_entropy(xx, ww, t, grad=False).token_loss))
+
+    for arr, grad in ((x, r.d_hidden), (w, r.d_weight)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            hstep = 1e-6 * max(1.0, abs(arr[idx]))
+            old = arr[idx]
+            arr[idx] = old + hstep
+            lp = objective(x, w)
+            arr[idx] = old - hstep
+            lm = objective(x, w)
+            arr[idx] = old
+            num[idx] = (lp - lm) / (2 * hstep)
+        err = np.max(np.abs(num - grad)) / max(1e-30, np.max(np.abs(grad)))
+        assert err <= 1e-6, err
+    xt = torch.tensor(x, dtype=torch.float64, requires_grad=True)
+    wt = torch.tensor(w, dtype=torch.float64, requires_grad=True)
+    tok = torch.nn.functional.cross_entropy(xt @ wt.T, torch.tensor(t), ignore_index=-100, reduction="none")
+    tok.backward(torch.tensor(u))
+    assert abs(r.loss - float(tok.sum().item())) <= 1e-12 * max(1.0, abs(r.loss))
+    np.testing.assert_allclose(r.token_loss, tok.detach().numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(r.d_hidden, xt.grad.numpy(), rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(r.d_weight, wt.grad.numpy(), rtol=1e-10, atol=1e-13)
+
+
 def check_zero_weight(orc, seed=3):
     rng = np.random.default_rng(seed)
     n, h, v = 9, 4, 11
@@ -212,6 +249,7 @@ def all_small_checks(orc):
     x, w, t = rand_instance(rng, 16, 8, 40, ignore=4)
     check_torch_reference(orc, x, w, t, row_block=5)
     check_finite_differences(orc)
+    check_per_token_reduction(orc)
     check_zero_weight(orc)
     check_logistic(orc)
     check_invariants(orc)

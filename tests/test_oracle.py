@@ -34,6 +34,10 @@ def test_finite_differences():
     pins.check_finite_differences(oracle)
 
 
+def test_per_token_reduction():
+    pins.check_per_token_reduction(oracle)
+
+
 def test_zero_weight_closed_form():
     pins.check_zero_weight(oracle)
 
@@ -104,6 +108,9 @@ MUTANTS = {
     "ring backward one-hot in wrong shard": ("gs[rows, t[rows] - s * vs] -= 1.0", "gs[rows, (t[rows] - s * vs + 1) % vs] -= 1.0"),
     "token loss sign": ("token_loss[r0 + rows] = lse_b[rows] - z[", "token_loss[r0 + rows] = -lse_b[rows] + z["),
     "row sample one-hot dropped": ("p[rows, t[rows]] -= 1.0\n    p *= np.where", "p *= np.where"),
+    "per-token scale ignores the token": ("scale = np.asarray(dloss, dtype=np.float64)",
+                                          "scale = np.full(t.shape, np.mean(dloss))"),
+    "per-token loss reported as a mean": ('if reduction in ("sum", "none"):', 'if reduction == "sum":'),
 }
 
 
