@@ -8,8 +8,9 @@ shards in ring order), inputs resident in HBM before the timed region. Prints
 one JSON line: tokens/s over the K timed steps, the fraction of MI355X dense
 bf16 MFMA peak the step reaches, peak device bytes, a roofline figure for the
 kernel with the largest share of the step (durations from HIP events recorded
-around every launch on the launching stream), and the CPU oracle timed on a
-bounded sample of the same workload on the host cores.
+around every launch on the launching stream, in a second pass of K steps),
+the forward / backward split per step (median and min), and the CPU oracle
+timed on a bounded sample of the same workload on the host cores.
 """
 from __future__ import annotations
 
@@ -101,6 +102,75 @@ def cpu_baseline(batch, target_s: float):
             "blas": blas, "cpu": cpu, "affinity_cores": len(os.sched_getaffinity(0))}
 
 
+def sclk_reader(dev_index: int):
+    """A callable returning the GPU's current shader clock in MHz (the starred
+    level of the amdgpu driver's pp_dpm_sclk for the device's PCI function), or
+    None where that file cannot be read."""
+    import glob
+    import torch
+    try:
+        pr = torch.cuda.get_device_properties(dev_index)
+        bdf = "%04x:%02x:%02x.0" % (pr.pci_domain_id, pr.pci_bus_id, pr.pci_device_id)
+    except Exception:
+        return None
+    path = None
+    for dev in glob.glob("/sys/class/drm/card*/device"):
+        try:
+            with open(os.path.join(dev, "uevent")) as f:
+                if f"PCI_SLOT_NAME={bdf}" in f.read():
+                    path = os.path.join(dev, "pp_dpm_sclk")
+                    break
+        except OSError:
+            continue
+    if path is None:
+        return None
+
+    def read():
+        try:
+            with open(path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        return float(line.split(":")[1].strip().rstrip("*").strip().lower().rstrip("mhz"))
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+    return read if read() is not None else None
+
+
+class ClockSampler:
+    """Samples the shader clock every few milliseconds on a host thread."""
+
+    def __init__(self, reader, period_s: float = 0.002):
+        import threading
+        self.reader, self.period, self.samples = reader, period_s, []
+        self._stop = threading.Event()
+        self._t = threading.Thread(target=self._run, daemon=True) if reader else None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self.reader()
+            if v is not None:
+                self.samples.append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self._t:
+            self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._t:
+            self._stop.set()
+            self._t.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        v = sorted(self.samples)
+        return {"source": "pp_dpm_sclk", "samples": len(v), "median_mhz": round(v[len(v) // 2], 1),
+                "min_mhz": round(v[0], 1), "max_mhz": round(v[-1], 1)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -175,8 +245,9 @@ def main() -> int:
     lce.trace_enable(1024)
     step()
     per_step = sum(e["launches"] for e in lce.trace_collect())
-    lce.trace_enable(per_step * args.steps + 16)
+    lce.trace_enable(0)
 
+    # the headline: K steps back to back, nothing else on the stream
     torch.cuda.synchronize(dev)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
@@ -187,8 +258,39 @@ def main() -> int:
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - wall0
     elapsed_ms = start.elapsed_time(end)
+
+    # per-kernel durations: the same K steps again with a HIP event pair
+    # recorded around every launch on the launching stream (the pairs add a
+    # little time between launches, so this pass is not the headline)
+    lce.trace_enable(per_step * args.steps + 16)
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start.record()
+    for _ in range(args.steps):
+        step()
+    t_end.record()
+    torch.cuda.synchronize(dev)
+    traced_ms = t_start.elapsed_time(t_end)
     kernels = lce.trace_collect()
     lce.trace_enable(0)
+
+    # per-step forward / backward split (median and min), with the shader
+    # clock sampled meanwhile; a separate pass so the headline loop above has
+    # no extra events in it
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    with ClockSampler(sclk_reader(0)) as clk:
+        for e0, e1, e2 in ev:
+            e0.record()
+            loss_s, lse_s = lce.forward(hidden, shards, targets, workspace=ws)
+            e1.record()
+            lce.backward(hidden, shards, targets, lse_s, dloss, workspace=ws, d_hidden=d_hidden, d_shards=d_shards)
+            e2.record()
+        torch.cuda.synchronize(dev)
+    fwd_ms = sorted(e0.elapsed_time(e1) for e0, e1, _ in ev)
+    bwd_ms = sorted(e1.elapsed_time(e2) for _, e1, e2 in ev)
+    step_ms = sorted(e0.elapsed_time(e2) for e0, _, e2 in ev)
+    split = {"fwd_ms_median": round(fwd_ms[len(fwd_ms) // 2], 4), "fwd_ms_min": round(fwd_ms[0], 4),
+             "bwd_ms_median": round(bwd_ms[len(bwd_ms) // 2], 4), "bwd_ms_min": round(bwd_ms[0], 4),
+             "step_ms_median": round(step_ms[len(step_ms) // 2], 4), "step_ms_min": round(step_ms[0], 4)}
     if not np.isfinite(loss_val):
         print(f"[bench] loss is not finite: {loss_val}", file=sys.stderr)
         return 1
@@ -203,7 +305,7 @@ def main() -> int:
     for e in kernels:
         avg_ms = e["total_ms"] / max(e["launches"], 1)
         kern.append({"kernel": e["name"], "launches_per_step": e["launches"] / args.steps,
-                     "avg_ms": round(avg_ms, 5), "share": round(e["total_ms"] / elapsed_ms, 4),
+                     "avg_ms": round(avg_ms, 5), "share": round(e["total_ms"] / traced_ms, 4),
                      "tflops": round(e["flops"] / (e["total_ms"] / 1e3) / 1e12, 2) if e["flops"] else None,
                      "gbs": round(e["bytes"] / (e["total_ms"] / 1e3) / 1e9, 1)})
     dom = max(kernels, key=lambda e: e["total_ms"])
@@ -248,6 +350,8 @@ def main() -> int:
         "strip_fp32_bytes": int(n) * int(vs) * 4,
         "loss": loss_val,
         "wall_s": round(wall, 3),
+        "timing": dict(split, traced_ms_per_step=round(traced_ms / args.steps, 4)),
+        "sclk": clk.summary(),
         "roofline": roof,
         "kernels": kern,
         "source_sha": kernel_source_sha(),

@@ -54,6 +54,14 @@ extern "C" {
 
 #define LCE_REDUCTION_MEAN 0 /* mean over tokens whose target != ignore_index */
 #define LCE_REDUCTION_SUM 1  /* sum over tokens whose target != ignore_index */
+#define LCE_REDUCTION_NONE 2 /* per token: token_loss is the result (loss gets
+                                their sum); backward takes a per-token dloss [N] */
+
+/* lce_dims.flags bits */
+#define LCE_FLAG_ACCUMULATE_DX 1 /* backward adds into d_hidden instead of overwriting it */
+#define LCE_FLAG_ACCUMULATE_DW 2 /* backward adds into the shard gradients */
+#define LCE_FLAG_BF16_GRADS 4    /* d_hidden and the shard gradients are bf16 (accumulated
+                                    in fp32 inside the workspace, rounded once at the end) */
 
 #define LCE_MAX_SHARDS 256
 
@@ -63,15 +71,17 @@ typedef struct lce_dims {
   int64_t vocab;        /* V >= 1, divisible by n_shards */
   int32_t n_shards;     /* P, 1..LCE_MAX_SHARDS */
   int32_t ignore_index; /* targets equal to this are skipped (e.g. -100) */
-  int32_t reduction;    /* LCE_REDUCTION_MEAN or LCE_REDUCTION_SUM */
-  int32_t reserved;     /* must be 0 */
+  int32_t reduction;    /* LCE_REDUCTION_MEAN, _SUM or _NONE */
+  int32_t flags;        /* LCE_FLAG_* bits; other bits must be 0 */
 } lce_dims;
 
 /*
  * Bytes of device workspace lce_forward and lce_backward need for `dims`.
  * Pure host function. The size is bounded independently of V: it holds
  * per-token state (O(N)) and two gradient chunks of at most 16384 x 8192 bf16
- * (fixed-size, whatever N and V), never a logit strip.
+ * (fixed-size, whatever N and V), never a logit strip; with
+ * LCE_FLAG_BF16_GRADS also fp32 accumulators for d_hidden (N x H) and one
+ * gradient chunk (at most 8192 x H).
  * Returns 0 if dims is invalid.
  */
 LCE_API size_t lce_workspace_bytes(const lce_dims* dims);
@@ -88,12 +98,13 @@ LCE_API size_t lce_workspace_bytes(const lce_dims* dims);
  *               [0, V) that is not ignore_index makes that token's loss NaN
  *               (and so the mean); no host synchronization is done to detect it.
  *  loss         device fp32 scalar, written: mean (or sum) over non-ignored
- *               tokens; NaN for a mean over zero tokens.
+ *               tokens; NaN for a mean over zero tokens. With
+ *               LCE_REDUCTION_NONE the sum (token_loss is then the result).
  *  lse          device fp32 [N], written: log-sum-exp of each token's full
  *               logit row (every token, ignored ones included). Keep it for
  *               lce_backward: it is the only state backward needs.
- *  token_loss   device fp32 [N] or NULL; written: lse - target logit, 0 for
- *               ignored tokens.
+ *  token_loss   device fp32 [N] or NULL (required for LCE_REDUCTION_NONE);
+ *               written: lse - target logit, 0 for ignored tokens.
  *  workspace    device buffer of at least lce_workspace_bytes(dims) bytes.
  */
 LCE_API int lce_forward(const lce_dims* dims, const void* hidden, const void* const* w_shards, const int32_t* shard_order,
@@ -105,17 +116,20 @@ LCE_API int lce_forward(const lce_dims* dims, const void* hidden, const void* co
  * from the saved normalizer.
  *  hidden, w_shards, shard_order, targets   as for lce_forward
  *  lse          device fp32 [N] from lce_forward on the same inputs
- *  dloss        device fp32 scalar: d(objective)/d(loss)
- *  d_hidden     device fp32 [N][H], overwritten with dloss * dL/dX.
- *               Rows of ignored tokens are exactly 0.
- *  d_w_shards   host array of P device pointers, each fp32 [V/P][H],
- *               overwritten with dloss * dL/dW for that shard.
+ *  dloss        device fp32 scalar: d(objective)/d(loss); for
+ *               LCE_REDUCTION_NONE device fp32 [N]: d(objective)/d(token_loss).
+ *  d_hidden     device fp32 [N][H] (bf16 with LCE_FLAG_BF16_GRADS), overwritten
+ *               with dL/dX scaled by dloss (added to it with
+ *               LCE_FLAG_ACCUMULATE_DX). Ignored tokens contribute exactly 0.
+ *  d_w_shards   host array of P device pointers, each fp32 [V/P][H] (bf16
+ *               with LCE_FLAG_BF16_GRADS), overwritten with that shard's
+ *               dL/dW scaled by dloss (added to with LCE_FLAG_ACCUMULATE_DW).
  *  workspace    as for lce_forward (the forward's contents are not needed).
  * A target outside [0, V) that is not ignore_index makes every output NaN.
  */
 LCE_API int lce_backward(const lce_dims* dims, const void* hidden, const void* const* w_shards, const int32_t* shard_order,
-                 const int32_t* targets, const float* lse, const float* dloss, float* d_hidden,
-                 float* const* d_w_shards, void* workspace, size_t workspace_bytes, void* stream);
+                 const int32_t* targets, const float* lse, const float* dloss, void* d_hidden,
+                 void* const* d_w_shards, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * One ring round at a time (same page, section 3.2 and Fig. 3: in each of
@@ -154,23 +168,53 @@ LCE_API int lce_backward(const lce_dims* dims, const void* hidden, const void* c
  *
  * lce_bwd_round
  *  round, shard_index, hidden, w_shard, targets  as for lce_fwd_round.
- *  lse, dloss   as for lce_backward (round 0 reads dloss; the scale it
- *               derives is kept in the workspace for the later rounds).
- *  d_hidden     device fp32 [N][H]: round 0 overwrites it, later rounds add
- *               this shard's part, so after round P-1 it holds dL/dX.
- *  d_w_shard    device fp32 [V/P][H]: this shard's gradient, overwritten, or
- *               added to what it holds when accumulate_dw != 0 (a driver that
- *               sums a travelling partial, or accumulates over micro-batches).
+ *  lse, dloss   as for lce_backward (every round reads them).
+ *  d_hidden     as for lce_backward: round 0 overwrites it (or adds, with
+ *               LCE_FLAG_ACCUMULATE_DX), later rounds add this shard's part,
+ *               so after round P-1 it holds dL/dX. With LCE_FLAG_BF16_GRADS the
+ *               sum is kept in fp32 in the workspace and written to the bf16
+ *               d_hidden by round P-1 only.
+ *  d_w_shard    this shard's gradient, overwritten, or added to what it holds
+ *               when accumulate_dw != 0 or LCE_FLAG_ACCUMULATE_DW is set (a
+ *               driver that sums a travelling partial, or accumulates over
+ *               micro-batches); bf16 with LCE_FLAG_BF16_GRADS.
  * The forward's workspace contents are not needed by the backward rounds;
  * lce_fwd_round must not run between backward rounds on the same workspace.
  */
+/*
+ * Two ways to run the ring (same page, section 3.2: the ring can circulate
+ * either the weight shards or the activations). The calls above serve both:
+ *  - weights move: rank r keeps its batch and workspace; in round k it gets
+ *    shard (r - k) mod P, and in the backward that shard's gradient partial
+ *    travels with it (accumulate_dw from round 1 on).
+ *  - activations move: rank r keeps shard r; in round k it gets batch
+ *    b = (r - k) mod P with that batch's targets, lse (backward), d_hidden
+ *    partial (backward) and the first lce_state_bytes(dims) bytes of the
+ *    batch's workspace, and calls with shard_index = r on them; its own shard
+ *    gradient stays put and accumulates over the batches (accumulate_dw from
+ *    round 1 on).
+ * lce_state_bytes: the leading workspace bytes that carry state from one call
+ * of a sequence to the next (forward state; the fp32 dX accumulator with
+ * LCE_FLAG_BF16_GRADS); the rest of the workspace is scratch. 0 if dims is
+ * invalid.
+ * lce_ring_payload: which payload moves fewer bytes per hop (one forward hop
+ * plus one backward hop): LCE_PAYLOAD_WEIGHTS (shard + gradient partial) or
+ * LCE_PAYLOAD_ACTIVATIONS (hidden, targets, lse, state and dX partial); the
+ * two byte counts are written to the non-NULL out-pointers. Pure host
+ * function; a negative status if dims is invalid.
+ */
+#define LCE_PAYLOAD_WEIGHTS 0
+#define LCE_PAYLOAD_ACTIVATIONS 1
+LCE_API size_t lce_state_bytes(const lce_dims* dims);
+LCE_API int lce_ring_payload(const lce_dims* dims, size_t* weight_bytes, size_t* activation_bytes);
+
 LCE_API int lce_fwd_round(const lce_dims* dims, int round, int shard_index, const void* hidden, const void* w_shard,
                           const int32_t* targets, void* workspace, size_t workspace_bytes, void* stream);
 LCE_API int lce_fwd_finish(const lce_dims* dims, const int32_t* targets, float* loss, float* lse, float* token_loss,
                            void* workspace, size_t workspace_bytes, void* stream);
 LCE_API int lce_bwd_round(const lce_dims* dims, int round, int shard_index, const void* hidden, const void* w_shard,
-                          const int32_t* targets, const float* lse, const float* dloss, float* d_hidden,
-                          float* d_w_shard, int accumulate_dw, void* workspace, size_t workspace_bytes, void* stream);
+                          const int32_t* targets, const float* lse, const float* dloss, void* d_hidden,
+                          void* d_w_shard, int accumulate_dw, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Kernel timing trace, for measurement (off by default).

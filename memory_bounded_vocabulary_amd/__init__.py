@@ -22,16 +22,17 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblce.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
-REDUCTIONS = {"mean": 0, "sum": 1}
-EXPORTED = ("lce_workspace_bytes", "lce_forward", "lce_backward", "lce_fwd_round", "lce_fwd_finish",
-            "lce_bwd_round", "lce_trace_enable", "lce_trace_collect", "lce_status_string", "lce_last_error",
+REDUCTIONS = {"mean": 0, "sum": 1, "none": 2}
+FLAG_ACCUMULATE_DX, FLAG_ACCUMULATE_DW, FLAG_BF16_GRADS = 1, 2, 4
+EXPORTED = ("lce_workspace_bytes", "lce_forward", "lce_backward", "lce_state_bytes", "lce_ring_payload",
+            "lce_fwd_round", "lce_fwd_finish", "lce_bwd_round", "lce_trace_enable", "lce_trace_collect", "lce_status_string", "lce_last_error",
             "lce_version")
 
 
 class Dims(ctypes.Structure):
     _fields_ = [("n_tokens", ctypes.c_int64), ("hidden", ctypes.c_int64), ("vocab", ctypes.c_int64),
                 ("n_shards", ctypes.c_int32), ("ignore_index", ctypes.c_int32),
-                ("reduction", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("reduction", ctypes.c_int32), ("flags", ctypes.c_int32)]
 
 
 class TraceEntry(ctypes.Structure):
@@ -67,6 +68,10 @@ def lib() -> ctypes.CDLL:
                                ctypes.c_size_t, vp]
     L.lce_backward.restype = ctypes.c_int
     ci, sz = ctypes.c_int, ctypes.c_size_t
+    L.lce_state_bytes.argtypes = [dimp]
+    L.lce_state_bytes.restype = sz
+    L.lce_ring_payload.argtypes = [dimp, ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    L.lce_ring_payload.restype = ctypes.c_int
     L.lce_fwd_round.argtypes = [dimp, ci, ci, vp, vp, vp, vp, sz, vp]
     L.lce_fwd_round.restype = ctypes.c_int
     L.lce_fwd_finish.argtypes = [dimp, vp, vp, vp, vp, vp, sz, vp]
@@ -89,13 +94,13 @@ def lib() -> ctypes.CDLL:
 
 
 def make_dims(n_tokens: int, hidden: int, vocab: int, n_shards: int, ignore_index: int = -100,
-              reduction: str = "mean") -> Dims:
-    return Dims(n_tokens, hidden, vocab, n_shards, ignore_index, REDUCTIONS[reduction], 0)
+              reduction: str = "mean", flags: int = 0) -> Dims:
+    return Dims(n_tokens, hidden, vocab, n_shards, ignore_index, REDUCTIONS[reduction], flags)
 
 
 def workspace_bytes(n_tokens: int, hidden: int, vocab: int, n_shards: int, ignore_index: int = -100,
-                    reduction: str = "mean") -> int:
-    d = make_dims(n_tokens, hidden, vocab, n_shards, ignore_index, reduction)
+                    reduction: str = "mean", flags: int = 0) -> int:
+    d = make_dims(n_tokens, hidden, vocab, n_shards, ignore_index, reduction, flags)
     return int(lib().lce_workspace_bytes(ctypes.byref(d)))
 
 
@@ -121,22 +126,42 @@ def _stream(stream) -> int:
     return int(s.cuda_stream)
 
 
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
 def _require_cuda(*tensors) -> None:
     for t in tensors:
         if not t.is_cuda:
             raise ValueError("lce runs on the GPU only: every tensor must be a cuda tensor")
 
 
+def state_bytes(dims: Dims) -> int:
+    """Leading workspace bytes that carry state between the calls of a round sequence."""
+    return int(lib().lce_state_bytes(ctypes.byref(dims)))
+
+
+def ring_payload(dims: Dims) -> Tuple[str, int, int]:
+    """('weights' | 'activations', weight bytes per hop, activation bytes per hop)."""
+    w, x = ctypes.c_size_t(), ctypes.c_size_t()
+    r = lib().lce_ring_payload(ctypes.byref(dims), ctypes.byref(w), ctypes.byref(x))
+    if r < 0:
+        _check(r)
+    return ("activations" if r == 1 else "weights"), int(w.value), int(x.value)
+
+
 def alloc_workspace(n_tokens: int, hidden: int, vocab: int, n_shards: int, device=None, ignore_index: int = -100,
-                    reduction: str = "mean"):
+                    reduction: str = "mean", flags: int = 0):
     import torch
-    nbytes = workspace_bytes(n_tokens, hidden, vocab, n_shards, ignore_index, reduction)
+    nbytes = workspace_bytes(n_tokens, hidden, vocab, n_shards, ignore_index, reduction, flags)
     return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device or "cuda")
 
 
 def forward(hidden, shards: Sequence, targets, ignore_index: int = -100, order: Optional[Sequence[int]] = None,
             reduction: str = "mean", workspace=None, token_loss: bool = False, stream=None):
-    """Loss and saved normalizer; returns (loss, lse) or (loss, lse, token_loss)."""
+    """Loss and saved normalizer; returns (loss, lse) or (loss, lse, token_loss).
+
+    reduction "none" always returns the token losses (loss is then their sum)."""
     import torch
     _require_cuda(hidden, targets, *shards)
     n, h = hidden.shape
@@ -145,45 +170,61 @@ def forward(hidden, shards: Sequence, targets, ignore_index: int = -100, order: 
     d = make_dims(n, h, v, p, ignore_index, reduction)
     if workspace is None:
         workspace = alloc_workspace(n, h, v, p, hidden.device, ignore_index, reduction)
+    token_loss = token_loss or reduction == "none"
     loss = torch.empty((), dtype=torch.float32, device=hidden.device)
     lse = torch.empty(n, dtype=torch.float32, device=hidden.device)
     tl = torch.empty(n, dtype=torch.float32, device=hidden.device) if token_loss else None
     st = lib().lce_forward(ctypes.byref(d), hidden.data_ptr(), _ptr_array([s.data_ptr() for s in shards]),
                            _order_array(order), targets.data_ptr(), loss.data_ptr(), lse.data_ptr(),
                            tl.data_ptr() if tl is not None else None, workspace.data_ptr(),
-                           workspace.numel() * workspace.element_size(), _stream(stream))
+                           _nbytes(workspace), _stream(stream))
     _check(st)
     return (loss, lse, tl) if token_loss else (loss, lse)
 
 
 def backward(hidden, shards: Sequence, targets, lse, dloss, ignore_index: int = -100,
              order: Optional[Sequence[int]] = None, reduction: str = "mean", workspace=None,
-             d_hidden=None, d_shards: Optional[List] = None, stream=None) -> Tuple[object, List]:
-    """Gradients (d_hidden fp32 [N][H], [d_shard fp32 [V/P][H]]) of dloss * loss."""
+             d_hidden=None, d_shards: Optional[List] = None, accumulate: bool = False,
+             grad_dtype=None, stream=None) -> Tuple[object, List]:
+    """Gradients (d_hidden [N][H], [d_shard [V/P][H]]) of the loss scaled by dloss.
+
+    dloss: scalar (mean / sum) or fp32 [N] (reduction "none"). grad_dtype:
+    torch.float32 (default) or torch.bfloat16 (accumulated in fp32, rounded
+    once). accumulate: add into the given d_hidden / d_shards."""
     import torch
     _require_cuda(hidden, targets, lse, *shards)
     n, h = hidden.shape
     p = len(shards)
     vs = shards[0].shape[0]
-    d = make_dims(n, h, p * vs, p, ignore_index, reduction)
+    grad_dtype = torch.float32 if grad_dtype is None else grad_dtype
+    if grad_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("grad_dtype must be torch.float32 or torch.bfloat16")
+    flags = FLAG_BF16_GRADS if grad_dtype == torch.bfloat16 else 0
+    if accumulate:
+        if d_hidden is None or d_shards is None:
+            raise ValueError("accumulate needs the d_hidden and d_shards to add into")
+        flags |= FLAG_ACCUMULATE_DX | FLAG_ACCUMULATE_DW
+    d = make_dims(n, h, p * vs, p, ignore_index, reduction, flags)
     if workspace is None:
-        workspace = alloc_workspace(n, h, p * vs, p, hidden.device, ignore_index, reduction)
+        workspace = alloc_workspace(n, h, p * vs, p, hidden.device, ignore_index, reduction, flags)
     if not torch.is_tensor(dloss):
         dloss = torch.tensor(float(dloss), dtype=torch.float32, device=hidden.device)
+    if reduction == "none" and dloss.numel() != n:
+        raise ValueError("reduction 'none' takes a per-token dloss of N elements")
+    _require_cuda(dloss)
     if d_hidden is None:
-        d_hidden = torch.empty((n, h), dtype=torch.float32, device=hidden.device)
+        d_hidden = torch.empty((n, h), dtype=grad_dtype, device=hidden.device)
     if d_shards is None:
-        d_shards = [torch.empty((vs, h), dtype=torch.float32, device=hidden.device) for _ in range(p)]
+        d_shards = [torch.empty((vs, h), dtype=grad_dtype, device=hidden.device) for _ in range(p)]
+    for t in (d_hidden, *d_shards):
+        if t.dtype != grad_dtype or not t.is_contiguous():
+            raise ValueError(f"gradient buffers must be contiguous {grad_dtype}")
     st = lib().lce_backward(ctypes.byref(d), hidden.data_ptr(), _ptr_array([s.data_ptr() for s in shards]),
                             _order_array(order), targets.data_ptr(), lse.data_ptr(), dloss.data_ptr(),
                             d_hidden.data_ptr(), _ptr_array([g.data_ptr() for g in d_shards]),
-                            workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream))
+                            workspace.data_ptr(), _nbytes(workspace), _stream(stream))
     _check(st)
     return d_hidden, d_shards
-
-
-def _nbytes(t) -> int:
-    return t.numel() * t.element_size()
 
 
 def fwd_round(dims: Dims, round_: int, shard_index: int, hidden, shard, targets, workspace, stream=None) -> None:

@@ -33,6 +33,7 @@ constexpr int64_t kVocabChunkMax = 8192;   // vocabulary rows per backward chunk
 constexpr int64_t kTokenChunkMax = 16384;  // tokens per backward chunk
 constexpr int kMaxSplits = 16;             // forward vocabulary splits per shard
 constexpr int kTargetWorkgroups = 256;     // one per compute unit
+constexpr int kKnownFlags = LCE_FLAG_ACCUMULATE_DX | LCE_FLAG_ACCUMULATE_DW | LCE_FLAG_BF16_GRADS;
 
 thread_local std::string g_last_error;
 
@@ -59,8 +60,10 @@ struct Plan {
   int64_t vs_pad, vcs, ncs;
   // forward workspace
   size_t off_state, off_yt, off_part, off_counters, fwd_bytes;
-  // backward workspace
-  size_t off_gscale, off_g, g_bytes, bwd_bytes;
+  // backward workspace (off_dx32 / off_dw32: fp32 accumulators for bf16 gradients)
+  size_t off_gscale, off_g, g_bytes, off_dx32, off_dw32, bwd_bytes;
+  size_t state_bytes;  // leading bytes that carry state from one call of a sequence to the next
+  bool bf16_grads;
   size_t bytes;
 };
 
@@ -74,10 +77,9 @@ int check_dims(const lce_dims* d) {
   if (d->vocab % d->n_shards)
     return fail(LCE_ERR_INVALID_ARG, "vocab (%lld) is not divisible by n_shards (%d)", (long long)d->vocab,
                 d->n_shards);
-  if (d->reduction != LCE_REDUCTION_MEAN && d->reduction != LCE_REDUCTION_SUM)
-    return fail(LCE_ERR_INVALID_ARG, "reduction must be LCE_REDUCTION_MEAN or LCE_REDUCTION_SUM (got %d)",
-                d->reduction);
-  if (d->reserved != 0) return fail(LCE_ERR_INVALID_ARG, "reserved must be 0");
+  if (d->reduction != LCE_REDUCTION_MEAN && d->reduction != LCE_REDUCTION_SUM && d->reduction != LCE_REDUCTION_NONE)
+    return fail(LCE_ERR_INVALID_ARG, "reduction must be LCE_REDUCTION_MEAN, _SUM or _NONE (got %d)", d->reduction);
+  if (d->flags & ~kKnownFlags) return fail(LCE_ERR_INVALID_ARG, "unknown flag bits 0x%x", d->flags & ~kKnownFlags);
   if (d->hidden % 64) return fail(LCE_ERR_UNSUPPORTED, "hidden (%lld) must be a multiple of 64", (long long)d->hidden);
   const int64_t vs = d->vocab / d->n_shards;
   const int64_t lim = int64_t(1) << 31;
@@ -121,12 +123,27 @@ Plan make_plan(const lce_dims* d) {
   o = align256(o + size_t(p.token_blocks + 1) * 4);
   p.fwd_bytes = o;
 
+  // Backward. What persists between the calls of one sequence sits first
+  // (the bf16 gradients' dX accumulator), so the state of a sequence is always
+  // a prefix of the workspace: state_bytes.
   o = 0;
+  p.bf16_grads = (d->flags & LCE_FLAG_BF16_GRADS) != 0;
+  p.off_dx32 = p.off_dw32 = 0;
+  if (p.bf16_grads) {
+    p.off_dx32 = o;
+    o = align256(o + size_t(p.N) * p.H * 4);
+  }
+  const size_t bwd_state = o;
   p.off_gscale = o;
   o = align256(o + 16);
   p.g_bytes = align256(size_t(p.ncs) * p.vcs * 2);
   p.off_g = o;  // two G chunks: consecutive backward units alternate
   o += 2 * p.g_bytes;
+  if (p.bf16_grads) {
+    p.off_dw32 = o;
+    o = align256(o + size_t(p.vcs) * p.H * 4);
+  }
+  p.state_bytes = std::max(p.fwd_bytes, bwd_state);
   p.bwd_bytes = o;
   p.bytes = std::max(p.fwd_bytes, p.bwd_bytes);
   return p;
@@ -172,9 +189,9 @@ int hip_status(hipError_t e, const char* what) {
 }
 
 // ---- optional per-launch event trace (see lce_trace_enable) ----
-enum Kind { kTargetLogit, kFwdRound, kFinalize, kBwdScale, kBwdG, kBwdStep, kGradGemm, kKinds };
+enum Kind { kTargetLogit, kFwdRound, kFinalize, kBwdScale, kBwdG, kBwdStep, kGradGemm, kConvert, kKinds };
 const char* const kKindName[kKinds] = {"target_logit", "fwd_round", "finalize", "bwd_scale", "bwd_g", "bwd_step",
-                                       "grad_gemm"};
+                                       "grad_gemm",    "bf16_convert"};
 
 struct Trace {
   std::vector<hipEvent_t> ev;  // pairs: [2i] before, [2i+1] after launch i
@@ -261,20 +278,29 @@ int run_fwd_rounds(const Plan& p, const lce::FwdArgs& a, const lce::ShardTable& 
 struct Unit {
   int sh, v0, vc, vc_pad, n0, nc, nc_pad;
   const uint16_t* W;  // the shard
-  float* dW;          // its gradient
+  float* dW;          // fp32 target of the dW contraction for rows v0.. (output, or the chunk accumulator)
+  uint16_t* dW_bf16;  // bf16 gradient rows v0.. (LCE_FLAG_BF16_GRADS), else NULL
   int acc_dx, acc_dw;
+  bool chunk_first, chunk_last;  // first / last unit of its (shard, vocabulary chunk)
 };
 
 // The units of one shard, in order; acc_dx/acc_dw set from `dx_written`
 // (per token chunk: has dX been written yet in this backward) and `acc_dw`.
-void shard_units(const Plan& p, int sh, const uint16_t* W, float* dW, std::vector<bool>& dx_written, bool acc_dw,
-                 std::vector<Unit>& out) {
+void shard_units(const Plan& p, int sh, const uint16_t* W, void* dW_out, char* ws, std::vector<bool>& dx_written,
+                 bool acc_dw, std::vector<Unit>& out) {
   for (int64_t v0 = 0; v0 < p.Vs; v0 += p.vcs) {
     const int vc = int(std::min<int64_t>(p.vcs, p.Vs - v0));
     for (int64_t n0 = 0; n0 < p.N; n0 += p.ncs) {
       const int nc = int(std::min<int64_t>(p.ncs, p.N - n0));
       const size_t nchunk = size_t(n0 / p.ncs);
-      Unit u{sh, int(v0), vc, int(round_up(vc, kTile)), int(n0), nc, int(round_up(nc, kTile)), W, dW, 0, 0};
+      Unit u{sh, int(v0), vc, int(round_up(vc, kTile)), int(n0), nc, int(round_up(nc, kTile)), W,
+             nullptr, nullptr, 0, 0, n0 == 0, n0 + p.ncs >= p.N};
+      if (p.bf16_grads) {
+        u.dW = reinterpret_cast<float*>(ws + p.off_dw32);
+        u.dW_bf16 = static_cast<uint16_t*>(dW_out) + size_t(v0) * p.H;
+      } else {
+        u.dW = static_cast<float*>(dW_out) + size_t(v0) * p.H;
+      }
       u.acc_dx = dx_written[nchunk] ? 1 : 0;
       dx_written[nchunk] = true;
       u.acc_dw = (acc_dw || n0 > 0) ? 1 : 0;
@@ -283,8 +309,18 @@ void shard_units(const Plan& p, int sh, const uint16_t* W, float* dW, std::vecto
   }
 }
 
-int run_bwd_scale(const Plan& p, const lce_dims* d, const int32_t* targets, const float* dloss, float* gscale,
-                  hipStream_t s) {
+// g = dloss / n_valid (mean) or dloss (sum) into the workspace; for
+// LCE_REDUCTION_NONE nothing runs and the per-token dloss is read directly.
+int run_bwd_scale(const Plan& p, const lce_dims* d, const int32_t* targets, const float* dloss, char* ws,
+                  const float** g, int* g_per_token, hipStream_t s) {
+  if (d->reduction == LCE_REDUCTION_NONE) {
+    *g = dloss;
+    *g_per_token = 1;
+    return LCE_OK;
+  }
+  float* gscale = reinterpret_cast<float*>(ws + p.off_gscale);
+  *g = gscale;
+  *g_per_token = 0;
   return hip_status(traced(kBwdScale, 0.0, 4.0 * double(p.N), s,
                            [&] {
                              return lce::launch_bwd_scale(targets, int(p.N), d->ignore_index, dloss, d->reduction,
@@ -293,12 +329,34 @@ int run_bwd_scale(const Plan& p, const lce_dims* d, const int32_t* targets, cons
                     "scale");
 }
 
+int run_convert(bool widen, const void* src, void* dst, int64_t rows, int64_t cols, hipStream_t s) {
+  const double n = double(rows) * double(cols);
+  return hip_status(traced(kConvert, 0.0, 6.0 * n, s,
+                           [&] {
+                             return widen ? lce::launch_widen_bf16(static_cast<const uint16_t*>(src),
+                                                                   static_cast<float*>(dst), rows, cols, s)
+                                          : lce::launch_narrow_bf16(static_cast<const float*>(src),
+                                                                    static_cast<uint16_t*>(dst), rows, cols, s);
+                           }),
+                    widen ? "widen" : "narrow");
+}
+
 // Launch j runs the gradient GEMMs of unit j - 1 and the recompute of unit j.
+// With bf16 gradients each vocabulary chunk's dW accumulates in the chunk
+// accumulator and is narrowed into the caller's buffer after the launch that
+// ends it (and, when accumulating, widened from it before the launch that
+// starts it).
 int run_bwd_units(const Plan& p, const lce_dims* d, const std::vector<Unit>& units, const uint16_t* X,
-                  const int32_t* targets, const float* lse, const float* gscale, float* d_hidden, char* ws,
-                  hipStream_t s) {
+                  const int32_t* targets, const float* lse, const float* g, int g_per_token, float* dX, bool acc_dw,
+                  char* ws, hipStream_t s) {
   const double dH = double(p.H);
   auto gbuf = [&](size_t u) { return reinterpret_cast<uint16_t*>(ws + p.off_g + (u & 1) * p.g_bytes); };
+  float* dw32 = reinterpret_cast<float*>(ws + p.off_dw32);
+  int st;
+  if (!units.empty() && units[0].dW_bf16 && acc_dw) {
+    st = run_convert(true, units[0].dW_bf16, dw32, units[0].vc, p.H, s);
+    if (st) return st;
+  }
   for (size_t j = 0; j <= units.size(); ++j) {
     lce::GradArgs ga{};
     lce::BwdGArgs ba{};
@@ -314,9 +372,9 @@ int run_bwd_units(const Plan& p, const lce_dims* d, const std::vector<Unit>& uni
       ga.Xc = X + size_t(u.n0) * p.H;
       ga.nc = u.nc;
       ga.H = int(p.H);
-      ga.dX = d_hidden + size_t(u.n0) * p.H;
+      ga.dX = dX + size_t(u.n0) * p.H;
       ga.acc_dx = u.acc_dx;
-      ga.dW = u.dW + size_t(u.v0) * p.H;
+      ga.dW = u.dW;
       ga.acc_dw = u.acc_dw;
       const double dnc = u.nc, dvc = u.vc, gb = 2.0 * double(u.nc_pad) * double(u.vc_pad);
       flops += 4.0 * dnc * dvc * dH;
@@ -329,7 +387,8 @@ int run_bwd_units(const Plan& p, const lce_dims* d, const std::vector<Unit>& uni
       ba.Ws = u.W;
       ba.targets = targets;
       ba.lse = lse;
-      ba.gscale = gscale;
+      ba.gscale = g;
+      ba.g_per_token = g_per_token;
       ba.G = gbuf(j);
       ba.N = int(p.N);
       ba.H = int(p.H);
@@ -349,13 +408,21 @@ int run_bwd_units(const Plan& p, const lce_dims* d, const std::vector<Unit>& uni
       bytes += 2.0 * dnc * dH + 2.0 * dvc * dH + 2.0 * double(u.nc_pad) * double(u.vc_pad) + 12.0 * dnc;
     }
     const Kind kind = j == 0 ? kBwdG : (j == units.size() ? kGradGemm : kBwdStep);
-    int st = hip_status(traced(kind, flops, bytes, s,
-                               [&] {
-                                 return lce::launch_bwd_step(j > 0 ? &ga : nullptr, j < units.size() ? &ba : nullptr,
-                                                             s);
-                               }),
-                        "backward step");
+    st = hip_status(traced(kind, flops, bytes, s,
+                           [&] {
+                             return lce::launch_bwd_step(j > 0 ? &ga : nullptr, j < units.size() ? &ba : nullptr,
+                                                         s);
+                           }),
+                    "backward step");
     if (st) return st;
+    if (j > 0 && units[j - 1].dW_bf16 && units[j - 1].chunk_last) {
+      st = run_convert(false, dw32, units[j - 1].dW_bf16, units[j - 1].vc, p.H, s);
+      if (st) return st;
+    }
+    if (j > 0 && j < units.size() && units[j].dW_bf16 && units[j].chunk_first && acc_dw) {
+      st = run_convert(true, units[j].dW_bf16, dw32, units[j].vc, p.H, s);
+      if (st) return st;
+    }
   }
   return LCE_OK;
 }
@@ -388,6 +455,25 @@ size_t lce_workspace_bytes(const lce_dims* dims) {
   return make_plan(dims).bytes;
 }
 
+size_t lce_state_bytes(const lce_dims* dims) {
+  if (check_dims(dims) != LCE_OK) return 0;
+  return make_plan(dims).state_bytes;
+}
+
+int lce_ring_payload(const lce_dims* d, size_t* weight_bytes, size_t* activation_bytes) {
+  int st = check_dims(d);
+  if (st) return st;
+  const Plan p = make_plan(d);
+  const size_t gb = p.bf16_grads ? 2 : 4;  // bytes of a gradient element
+  // one hop of the forward plus one of the backward
+  const size_t w = size_t(p.Vs) * p.H * 2 * 2 + size_t(p.Vs) * p.H * gb;
+  const size_t x = size_t(p.N) * p.H * 2 * 2 + size_t(p.N) * 4 * 2 + p.fwd_bytes + size_t(p.N) * 4 +
+                   size_t(p.N) * p.H * 4;
+  if (weight_bytes) *weight_bytes = w;
+  if (activation_bytes) *activation_bytes = x;
+  return x < w ? LCE_PAYLOAD_ACTIVATIONS : LCE_PAYLOAD_WEIGHTS;
+}
+
 int lce_forward(const lce_dims* d, const void* hidden, const void* const* w_shards, const int32_t* shard_order,
                 const int32_t* targets, float* loss, float* lse, float* token_loss, void* workspace,
                 size_t workspace_bytes, void* stream) {
@@ -395,6 +481,8 @@ int lce_forward(const lce_dims* d, const void* hidden, const void* const* w_shar
   int st = check_common(d, hidden, w_shards, targets, workspace, workspace_bytes, &p);
   if (st) return st;
   if (!loss || !lse) return fail(LCE_ERR_INVALID_ARG, "loss and lse must be non-NULL");
+  if (!token_loss && d->reduction == LCE_REDUCTION_NONE)
+    return fail(LCE_ERR_INVALID_ARG, "token_loss must be non-NULL for LCE_REDUCTION_NONE");
   if (!aligned16(lse) || (token_loss && !aligned16(token_loss)))
     return fail(LCE_ERR_UNSUPPORTED, "lse/token_loss not 16-byte aligned");
   int32_t order[LCE_MAX_SHARDS];
@@ -425,8 +513,8 @@ int lce_forward(const lce_dims* d, const void* hidden, const void* const* w_shar
 }
 
 int lce_backward(const lce_dims* d, const void* hidden, const void* const* w_shards, const int32_t* shard_order,
-                 const int32_t* targets, const float* lse, const float* dloss, float* d_hidden,
-                 float* const* d_w_shards, void* workspace, size_t workspace_bytes, void* stream) {
+                 const int32_t* targets, const float* lse, const float* dloss, void* d_hidden,
+                 void* const* d_w_shards, void* workspace, size_t workspace_bytes, void* stream) {
   Plan p;
   int st = check_common(d, hidden, w_shards, targets, workspace, workspace_bytes, &p);
   if (st) return st;
@@ -444,15 +532,25 @@ int lce_backward(const lce_dims* d, const void* hidden, const void* const* w_sha
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  float* gscale = reinterpret_cast<float*>(ws + p.off_gscale);
-  st = run_bwd_scale(p, d, targets, dloss, gscale, s);
+  const bool acc_dx = (d->flags & LCE_FLAG_ACCUMULATE_DX) != 0, acc_dw = (d->flags & LCE_FLAG_ACCUMULATE_DW) != 0;
+  const float* g = nullptr;
+  int g_per_token = 0;
+  st = run_bwd_scale(p, d, targets, dloss, ws, &g, &g_per_token, s);
   if (st) return st;
+  float* dx32 = p.bf16_grads ? reinterpret_cast<float*>(ws + p.off_dx32) : static_cast<float*>(d_hidden);
+  if (p.bf16_grads && acc_dx) {
+    st = run_convert(true, d_hidden, dx32, p.N, p.H, s);
+    if (st) return st;
+  }
   std::vector<Unit> units;
-  std::vector<bool> dx_written(size_t(ceil_div(p.N, p.ncs)), false);
+  std::vector<bool> dx_written(size_t(ceil_div(p.N, p.ncs)), acc_dx);
   for (int k = 0; k < d->n_shards; ++k)
-    shard_units(p, order[k], static_cast<const uint16_t*>(w_shards[order[k]]), d_w_shards[order[k]], dx_written, false,
-                units);
-  return run_bwd_units(p, d, units, static_cast<const uint16_t*>(hidden), targets, lse, gscale, d_hidden, ws, s);
+    shard_units(p, order[k], static_cast<const uint16_t*>(w_shards[order[k]]), d_w_shards[order[k]], ws, dx_written,
+                acc_dw, units);
+  st = run_bwd_units(p, d, units, static_cast<const uint16_t*>(hidden), targets, lse, g, g_per_token, dx32, acc_dw,
+                     ws, s);
+  if (st || !p.bf16_grads) return st;
+  return run_convert(false, dx32, d_hidden, p.N, p.H, s);
 }
 
 int lce_fwd_round(const lce_dims* d, int round, int shard_index, const void* hidden, const void* w_shard,
@@ -478,6 +576,8 @@ int lce_fwd_finish(const lce_dims* d, const int32_t* targets, float* loss, float
   if (st) return st;
   if (!targets || !loss || !lse || !workspace)
     return fail(LCE_ERR_INVALID_ARG, "targets, loss, lse and workspace must be non-NULL");
+  if (!token_loss && d->reduction == LCE_REDUCTION_NONE)
+    return fail(LCE_ERR_INVALID_ARG, "token_loss must be non-NULL for LCE_REDUCTION_NONE");
   if (!aligned16(targets) || !aligned16(lse) || (token_loss && !aligned16(token_loss)) || !aligned16(workspace))
     return fail(LCE_ERR_UNSUPPORTED, "targets/lse/token_loss/workspace not 16-byte aligned");
   const Plan p = make_plan(d);
@@ -491,7 +591,7 @@ int lce_fwd_finish(const lce_dims* d, const int32_t* targets, float* loss, float
 }
 
 int lce_bwd_round(const lce_dims* d, int round, int shard_index, const void* hidden, const void* w_shard,
-                  const int32_t* targets, const float* lse, const float* dloss, float* d_hidden, float* d_w_shard,
+                  const int32_t* targets, const float* lse, const float* dloss, void* d_hidden, void* d_w_shard,
                   int accumulate_dw, void* workspace, size_t workspace_bytes, void* stream) {
   Plan p;
   int st = check_round_args(d, round, shard_index, hidden, w_shard, targets, workspace, workspace_bytes, &p);
@@ -503,15 +603,24 @@ int lce_bwd_round(const lce_dims* d, int round, int shard_index, const void* hid
   g_last_error.clear();
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  float* gscale = reinterpret_cast<float*>(ws + p.off_gscale);
-  if (round == 0) {
-    st = run_bwd_scale(p, d, targets, dloss, gscale, s);
+  const bool acc_dx = round > 0 || (d->flags & LCE_FLAG_ACCUMULATE_DX) != 0;
+  const bool acc_dw = accumulate_dw != 0 || (d->flags & LCE_FLAG_ACCUMULATE_DW) != 0;
+  const float* g = nullptr;
+  int g_per_token = 0;
+  st = run_bwd_scale(p, d, targets, dloss, ws, &g, &g_per_token, s);
+  if (st) return st;
+  float* dx32 = p.bf16_grads ? reinterpret_cast<float*>(ws + p.off_dx32) : static_cast<float*>(d_hidden);
+  if (p.bf16_grads && round == 0 && acc_dx) {
+    st = run_convert(true, d_hidden, dx32, p.N, p.H, s);
     if (st) return st;
   }
   std::vector<Unit> units;
-  std::vector<bool> dx_written(size_t(ceil_div(p.N, p.ncs)), round > 0);
-  shard_units(p, shard_index, static_cast<const uint16_t*>(w_shard), d_w_shard, dx_written, accumulate_dw != 0, units);
-  return run_bwd_units(p, d, units, static_cast<const uint16_t*>(hidden), targets, lse, gscale, d_hidden, ws, s);
+  std::vector<bool> dx_written(size_t(ceil_div(p.N, p.ncs)), acc_dx);
+  shard_units(p, shard_index, static_cast<const uint16_t*>(w_shard), d_w_shard, ws, dx_written, acc_dw, units);
+  st = run_bwd_units(p, d, units, static_cast<const uint16_t*>(hidden), targets, lse, g, g_per_token, dx32, acc_dw,
+                     ws, s);
+  if (st || !p.bf16_grads || round != d->n_shards - 1) return st;
+  return run_convert(false, dx32, d_hidden, p.N, p.H, s);
 }
 
 int lce_trace_enable(int capacity) {

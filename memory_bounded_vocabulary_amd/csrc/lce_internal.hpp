@@ -46,10 +46,10 @@ struct BwdGArgs {
   const uint16_t* Ws;       // the unit's shard [Vs][H]
   const int* targets;
   const float* lse;
-  const float* gscale;      // device scalar g = dloss / n_valid (or dloss)
+  const float* gscale;      // g = dloss / n_valid (or dloss): gscale[0], or gscale[row] if g_per_token
   uint16_t* G;              // [nc_pad][vc_pad], pitch ldg
   int N, H, Vs, v0, vc, n0, nc, nc_pad, vc_pad;
-  int ignore_index, vocab_base, V, ldg;
+  int ignore_index, vocab_base, V, ldg, g_per_token;
   int n_tt, n_tv;           // set by the launcher
 };
 
@@ -67,5 +67,10 @@ struct GradArgs {
 // One launch: the gradient tiles of `gr` (may be NULL) and the recompute tiles
 // of `bg` (may be NULL); their G buffers must differ.
 hipError_t launch_bwd_step(const GradArgs* gr, const BwdGArgs* bg, hipStream_t st);
+
+// bf16 gradient outputs: rows x cols fp32 <-> bf16 (round to nearest even),
+// row pitch `cols` on both sides; cols a multiple of 8, pointers 16-byte aligned.
+hipError_t launch_widen_bf16(const uint16_t* src, float* dst, int64_t rows, int64_t cols, hipStream_t st);
+hipError_t launch_narrow_bf16(const float* src, uint16_t* dst, int64_t rows, int64_t cols, hipStream_t st);
 
 }  // namespace lce

@@ -382,7 +382,7 @@ __device__ __forceinline__ void recompute_g_tile(const BwdGArgs& a, int id, LCE_
         if (t < 0 || t >= a.V) {
           g[j] = __builtin_nanf("");
         } else {
-          g[j] = a.gscale[0];
+          g[j] = a.gscale[a.g_per_token ? row : 0];
           tcol[j] = t - (a.vocab_base + tv * kBM);
         }
       }
@@ -605,6 +605,43 @@ __global__ __launch_bounds__(256) void finalize_kernel(FwdArgs a) {
   if (threadIdx.x == 0) a.loss[0] = (float)(a.reduction == 0 ? s / (double)c : s);
 }
 
+// --------------------------------------------------------------------------
+// bf16 gradient outputs: the contractions accumulate in fp32 scratch; these
+// convert between that scratch and the caller's bf16 buffers, 8 elements per
+// thread with 16-byte accesses (round to nearest even on narrowing).
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void widen_bf16_kernel(const uint16_t* __restrict__ src, float* __restrict__ dst,
+                                                         int64_t n8) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
+    const u32x4 v = reinterpret_cast<const u32x4*>(src)[i];
+    float4 lo, hi;
+    lo.x = __uint_as_float(v[0] << 16);
+    lo.y = __uint_as_float(v[0] & 0xffff0000u);
+    lo.z = __uint_as_float(v[1] << 16);
+    lo.w = __uint_as_float(v[1] & 0xffff0000u);
+    hi.x = __uint_as_float(v[2] << 16);
+    hi.y = __uint_as_float(v[2] & 0xffff0000u);
+    hi.z = __uint_as_float(v[3] << 16);
+    hi.w = __uint_as_float(v[3] & 0xffff0000u);
+    reinterpret_cast<float4*>(dst)[2 * i] = lo;
+    reinterpret_cast<float4*>(dst)[2 * i + 1] = hi;
+  }
+}
+
+__global__ __launch_bounds__(256) void narrow_bf16_kernel(const float* __restrict__ src, uint16_t* __restrict__ dst,
+                                                          int64_t n8) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
+    const float4 lo = reinterpret_cast<const float4*>(src)[2 * i];
+    const float4 hi = reinterpret_cast<const float4*>(src)[2 * i + 1];
+    u32x4 v;
+    v[0] = pack_bf16x2(lo.x, lo.y);
+    v[1] = pack_bf16x2(lo.z, lo.w);
+    v[2] = pack_bf16x2(hi.x, hi.y);
+    v[3] = pack_bf16x2(hi.z, hi.w);
+    reinterpret_cast<u32x4*>(dst)[i] = v;
+  }
+}
+
 // ============================ host launchers ==============================
 static inline hipError_t last() { return hipGetLastError(); }
 
@@ -656,6 +693,25 @@ hipError_t launch_bwd_step(const GradArgs* gr, const BwdGArgs* bg, hipStream_t s
   }
   if (grad_slots + g_tiles == 0) return hipSuccess;
   hipLaunchKernelGGL(bwd_step_kernel, dim3(grad_slots + g_tiles), dim3(kThreads), 0, st, g, grad_slots, b, g_tiles);
+  return last();
+}
+
+static inline unsigned elementwise_blocks(int64_t n8) {
+  const int64_t b = (n8 + 255) / 256;
+  return (unsigned)(b < 4096 ? (b < 1 ? 1 : b) : 4096);  // grid-stride beyond 4096 blocks
+}
+
+hipError_t launch_widen_bf16(const uint16_t* src, float* dst, int64_t rows, int64_t cols, hipStream_t st) {
+  const int64_t n8 = rows * cols / 8;
+  if (n8 == 0) return hipSuccess;
+  hipLaunchKernelGGL(widen_bf16_kernel, dim3(elementwise_blocks(n8)), dim3(256), 0, st, src, dst, n8);
+  return last();
+}
+
+hipError_t launch_narrow_bf16(const float* src, uint16_t* dst, int64_t rows, int64_t cols, hipStream_t st) {
+  const int64_t n8 = rows * cols / 8;
+  if (n8 == 0) return hipSuccess;
+  hipLaunchKernelGGL(narrow_bf16_kernel, dim3(elementwise_blocks(n8)), dim3(256), 0, st, src, dst, n8);
   return last();
 }
 

@@ -37,8 +37,8 @@ def test_single_hip_runtime_in_process():
     assert len(paths) == 1, paths
 
 
-def _dims(n=256, h=128, v=1024, p=4, ignore=-100, red=0, reserved=0):
-    return Dims(n, h, v, p, ignore, red, reserved)
+def _dims(n=256, h=128, v=1024, p=4, ignore=-100, red=0, flags=0):
+    return Dims(n, h, v, p, ignore, red, flags)
 
 
 def _fwd(d, hidden=FAKE, shards=None, order=None, targets=FAKE, loss=FAKE, lse=FAKE, tl=None, ws=FAKE,
@@ -72,8 +72,8 @@ def _bwd(d, hidden=FAKE, lse=FAKE, dloss=FAKE, dx=FAKE, dws=None, ws=FAKE, ws_by
     (_dims(p=0), lce.ERR_INVALID_ARG),
     (_dims(p=257, v=257 * 4), lce.ERR_INVALID_ARG),
     (_dims(v=1000, p=3), lce.ERR_INVALID_ARG),
-    (_dims(red=2), lce.ERR_INVALID_ARG),
-    (_dims(reserved=1), lce.ERR_INVALID_ARG),
+    (_dims(flags=8), lce.ERR_INVALID_ARG),
+    (_dims(red=3), lce.ERR_INVALID_ARG),
     (_dims(h=100), lce.ERR_UNSUPPORTED),
     (_dims(n=1 << 22, h=1024), lce.ERR_UNSUPPORTED),
 ])
@@ -184,3 +184,46 @@ def test_round_entry_points_reject_bad_arguments():
     assert _fwd_round(d, ws_bytes=need - 1) == lce.ERR_WORKSPACE
     assert _fwd_finish(d, ws_bytes=need - 1) == lce.ERR_WORKSPACE
     assert _bwd_round(d, ws_bytes=need - 1) == lce.ERR_WORKSPACE
+
+
+def test_per_token_reduction_needs_token_loss():
+    d = _dims(red=2)
+    assert _fwd(d, tl=None) == lce.ERR_INVALID_ARG
+    assert "token_loss" in lce.lib().lce_last_error().decode()
+    assert _fwd_finish(d, tl=None) == lce.ERR_INVALID_ARG
+
+
+def test_bf16_gradient_workspace():
+    # fp32 accumulators for d_hidden (N x H) and one gradient chunk (<= 8192 x H)
+    n, h, v, p = 1000, 512, 8 * 20000, 8
+    plain = lce.workspace_bytes(n, h, v, p)
+    bf16 = lce.workspace_bytes(n, h, v, p, flags=lce.FLAG_BF16_GRADS)
+    assert n * h * 4 + 256 * h * 4 <= bf16 - plain <= n * h * 4 + 8192 * h * 4 + 1024
+    assert lce.workspace_bytes(n, h, v, p, flags=lce.FLAG_ACCUMULATE_DX | lce.FLAG_ACCUMULATE_DW) == plain
+
+
+def test_ring_payload_choice():
+    # one forward + one backward hop: a shard moves (V/P) H (2 + 2 + 4) bytes,
+    # a batch N H (2 + 2 + 4) bytes plus O(N) state: the smaller side moves
+    for name, n, h, v, p, want in [("long", 65536, 7168, 129280, 8, "weights"),
+                                   ("stress", 131071, 4096, 151936, 16, "weights"),
+                                   ("short batch", 1024, 4096, 128256, 8, "activations"),
+                                   ("many shards", 16384, 4096, 128256 * 4, 8, "activations")]:
+        choice, wb, xb = lce.ring_payload(lce.make_dims(n, h, v, p))
+        assert choice == want, (name, wb, xb)
+        assert wb == (v // p) * h * 8
+        assert n * h * 8 <= xb <= n * h * 8 + 256 * n + 4096  # state: up to 16 (m, z) pairs per token
+    assert lce.lib().lce_ring_payload(ctypes.byref(_dims(h=100)), None, None) == lce.ERR_UNSUPPORTED
+
+
+def test_state_bytes_is_a_prefix_of_the_workspace():
+    for flags in (0, lce.FLAG_BF16_GRADS):
+        d = lce.make_dims(5000, 1024, 8 * 3000, 8, flags=flags)
+        sb, wsb = lce.state_bytes(d), lce.workspace_bytes(5000, 1024, 8 * 3000, 8, flags=flags)
+        assert 0 < sb <= wsb
+        assert sb >= 8 * 5000  # at least one (m, z) pair per token
+        if flags:
+            assert sb >= 5000 * 1024 * 4  # the fp32 dX accumulator
+        else:
+            assert sb < 5000 * 1024  # O(N), no H-sized term
+    assert lce.state_bytes(_dims(v=1000, p=3)) == 0

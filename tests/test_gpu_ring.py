@@ -156,3 +156,74 @@ def test_accumulate_into_existing_gradient():
     e = rel_max(got, expect)
     say(f"accumulate: rel={e:.2e}")
     assert e <= GRAD_TOL
+
+
+ACT_RINGS = [
+    ("4 ranks", 600, 256, 4 * 300, 4),
+    ("3 ranks, two vocab chunks", 257, 64, 3 * 9000, 3),
+]
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["fp32", "bf16"])
+@pytest.mark.parametrize("case", ACT_RINGS, ids=[c[0] for c in ACT_RINGS])
+def test_activation_ring_simulation_parity(case, bf16):
+    """The other payload: rank r keeps shard r and its gradient; batch b visits
+    rank (b + k) mod P in round k, carrying its targets, lse, dX partial and the
+    first lce_state_bytes of its workspace, copied from rank to rank here."""
+    import torch
+    import memory_bounded_vocabulary_amd as lce
+    name, n, h, v, p = case
+    say("activation ring", name, dict(N=n, H=h, V=v, P=p, bf16=bf16))
+    w = BASE.with_dims(name=name, n_tokens=n, hidden=h, vocab=v, n_shards=p, ignore_frac=0.1, w_std=0.05)
+    weight = workloads.make(w, seed=60).weight
+    batches = [workloads.make(w, seed=61 + b, weight=weight) for b in range(p)]
+    dev = [to_device(b) for b in batches]
+    shards = dev[0][1]
+    flags = lce.FLAG_BF16_GRADS if bf16 else 0
+    dims = lce.make_dims(n, h, v, p, flags=flags)
+    sb = lce.state_bytes(dims)
+    ws = [lce.alloc_workspace(n, h, v, p, flags=flags) for _ in range(p)]  # rank r's own workspace
+
+    def hop():  # every rank passes the state it holds to rank r + 1
+        transit = [ws[r][:sb].clone() for r in range(p)]
+        for r in range(p):
+            ws[r][:sb].copy_(transit[(r - 1) % p])
+
+    for k in range(p):
+        if k:
+            hop()
+        for r in range(p):
+            b = (r - k) % p
+            lce.fwd_round(dims, k, r, dev[b][0], shards[r], dev[b][2], ws[r])
+    outs = [None] * p
+    for r in range(p):
+        b = (r - (p - 1)) % p
+        outs[b] = lce.fwd_finish(dims, dev[b][2], ws[r], token_loss=True)
+    dt = torch.bfloat16 if bf16 else torch.float32
+    dloss = torch.ones((), dtype=torch.float32, device="cuda")
+    dx = [torch.empty((n, h), dtype=dt, device="cuda") for _ in range(p)]       # travels with batch b
+    dws = [torch.empty((v // p, h), dtype=dt, device="cuda") for _ in range(p)]  # stays on rank r
+    for k in range(p):
+        if k:
+            hop()
+        for r in range(p):
+            b = (r - k) % p
+            lce.bwd_round(dims, k, r, dev[b][0], shards[r], dev[b][2], outs[b][1], dloss, dx[b], dws[r], k > 0, ws[r])
+    torch.cuda.synchronize()
+
+    vs = v // p
+    w64 = oracle.bf16_to_f64(weight)
+    w_shards = [w64[s * vs:(s + 1) * vs] for s in range(p)]
+    dw_sum = np.zeros_like(w64)
+    for b, bt in enumerate(batches):
+        ref = oracle.ring_fold(oracle.bf16_to_f64(bt.hidden), w_shards, [(b + k) % p for k in range(p)], bt.targets)
+        dw_sum += ref.d_weight
+        loss, lse, tl = outs[b]
+        got = {"loss": float(loss.item()), "lse": lse.cpu().numpy().astype(np.float64),
+               "token_loss": tl.cpu().numpy().astype(np.float64),
+               "d_hidden": dx[b].float().cpu().numpy().astype(np.float64), "d_weight": ref.d_weight}
+        compare(got, ref, f"{name} batch {b}")
+    got_dw = np.concatenate([d.float().cpu().numpy() for d in dws]).astype(np.float64)
+    e = rel_max(got_dw, dw_sum)
+    say(f"{name}: stationary dW rel={e:.2e}")
+    assert e <= GRAD_TOL
