@@ -171,6 +171,62 @@ class ClockSampler:
                 "min_mhz": round(v[0], 1), "max_mhz": round(v[-1], 1)}
 
 
+def materialized(hidden, shards, targets, args, out, dev):
+    """The plain path the method replaces, on the same inputs: the full logits
+    from a bf16 linear layer, cast to fp32, torch's cross-entropy (mean over
+    non-ignored tokens), gradients by autograd. A measurement beside the
+    library, not a code path of it; its peak bytes and step time against the
+    library's give the shape of the pages' memory/time claim."""
+    import torch
+    import torch.nn.functional as F
+    w = torch.cat(list(shards)).detach()
+    del shards
+    torch.cuda.synchronize(dev)
+    torch.cuda.empty_cache()
+    base = torch.cuda.memory_allocated(dev)
+    x = hidden.detach().clone().requires_grad_(True)
+    wp = w.clone().requires_grad_(True)
+    tl = targets.long()
+    io = torch.cuda.memory_allocated(dev) - base
+
+    def step():
+        x.grad = None
+        wp.grad = None
+        logits = F.linear(x, wp)
+        loss = F.cross_entropy(logits.float(), tl, ignore_index=-100)
+        loss.backward()
+        return loss
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        loss = step()
+    e1.record()
+    torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1) / args.steps
+    peak = torch.cuda.max_memory_allocated(dev) - base
+    grads = x.grad.numel() * x.grad.element_size() + wp.grad.numel() * wp.grad.element_size()
+    res = {
+        "what": "bf16 linear -> fp32 cross_entropy (mean, ignore_index=-100) -> autograd; bf16 gradients",
+        "ms_per_step": round(ms, 4),
+        "tokens_per_s": round(x.shape[0] / (ms / 1e3), 1),
+        "loss": float(loss.item()),
+        "peak_bytes": int(peak),
+        "transient_bytes": int(peak - io - grads),
+        "lce_ms_per_step": out["ms_per_step"],
+        "lce_transient_bytes": out["transient_bytes"],
+        "time_ratio_lce_over_materialized": round(out["ms_per_step"] / ms, 4),
+        "transient_reduction": round(1.0 - out["transient_bytes"] / max(1, peak - io - grads), 4),
+    }
+    del x, wp, w
+    torch.cuda.empty_cache()
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -180,6 +236,9 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--compare-materialized", action="store_true",
+                    help="also time the plain materialising path (bf16 linear, fp32 cross-entropy, autograd) on "
+                         "the same inputs and report its step time and peak bytes beside this library's")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="copy this many MiB device-to-device once before timing (a plain copy of known size, "
                          "for scaling hardware byte counters)")
@@ -357,6 +416,9 @@ def main() -> int:
         "source_sha": kernel_source_sha(),
         "host": platform.node(),
     }
+    if args.compare_materialized:
+        print("[bench] timing the materialising path", file=sys.stderr, flush=True)
+        out["materialized"] = materialized(hidden, shards, targets, args, out, dev)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(batch, args.cpu_seconds)
