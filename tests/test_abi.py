@@ -227,3 +227,29 @@ def test_state_bytes_is_a_prefix_of_the_workspace():
         else:
             assert sb < 5000 * 1024  # O(N), no H-sized term
     assert lce.state_bytes(_dims(v=1000, p=3)) == 0
+
+
+def test_last_error_is_per_thread():
+    import threading
+    results = {}
+
+    def work(i):
+        d = _dims(v=1000 + 3 * i + 1, p=3) if i % 2 else _dims(h=100 + 2 * i)  # never a valid shape
+        msgs = set()
+        for _ in range(200):
+            st = _fwd(d, ws_bytes=1 << 30)
+            msgs.add((st, lce.lib().lce_last_error().decode()))
+        results[i] = msgs
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(6)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    for i, msgs in results.items():
+        assert len(msgs) == 1, (i, msgs)          # never another thread's message
+        st, msg = next(iter(msgs))
+        if i % 2:
+            assert st == lce.ERR_INVALID_ARG and "divisible" in msg
+        else:
+            assert st == lce.ERR_UNSUPPORTED and "multiple of 64" in msg
