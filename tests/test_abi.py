@@ -253,3 +253,21 @@ def test_last_error_is_per_thread():
             assert st == lce.ERR_INVALID_ARG and "divisible" in msg
         else:
             assert st == lce.ERR_UNSUPPORTED and "multiple of 64" in msg
+
+
+def test_plain_c_caller(tmp_path):
+    """The ABI from C: compile tests/c_abi_check.c with gcc against include/lce.h,
+    link the built library, run it (host-side checks only)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    lib_dir = os.path.dirname(lce.LIB_PATH)
+    exe = str(tmp_path / "c_abi_check")
+    subprocess.run([gcc, "-std=c11", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    os.path.join(ROOT, "tests", "c_abi_check.c"), "-o", exe, "-L", lib_dir, "-llce",
+                    f"-Wl,-rpath,{lib_dir}"], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert "c abi ok" in r.stdout

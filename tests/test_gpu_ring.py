@@ -227,3 +227,60 @@ def test_activation_ring_simulation_parity(case, bf16):
     e = rel_max(got_dw, dw_sum)
     say(f"{name}: stationary dW rel={e:.2e}")
     assert e <= GRAD_TOL
+
+
+VARIANTS = [
+    # reduction, bf16 gradients, accumulate into prior contents
+    ("mean", True, False),
+    ("none", False, False),
+    ("sum", True, True),
+    ("mean", False, True),
+]
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=["-".join(map(str, v)) for v in VARIANTS])
+def test_round_variants_match_whole_pass(variant):
+    """Per-round backward with the flags and reductions equals the whole-pass
+    backward with the same ones, bit for bit (same launches, same data)."""
+    import torch
+    import memory_bounded_vocabulary_amd as lce
+    reduction, bf16, acc = variant
+    w = BASE.with_dims(name="round variants", n_tokens=16384 + 300, hidden=64, vocab=3 * 3000, n_shards=3,
+                       ignore_frac=0.1, w_std=0.3)
+    b = workloads.make(w, seed=12)
+    hidden, shards, targets = to_device(b)
+    say("round variants", variant)
+    n, h, v, p = w.n_tokens, w.hidden, w.vocab, w.n_shards
+    order = [1, 2, 0]
+    dt = torch.bfloat16 if bf16 else torch.float32
+    flags = (lce.FLAG_BF16_GRADS if bf16 else 0) | (lce.FLAG_ACCUMULATE_DX | lce.FLAG_ACCUMULATE_DW if acc else 0)
+    out = lce.forward(hidden, shards, targets, order=order, reduction=reduction, token_loss=True)
+    lse = out[1]
+    gen = torch.Generator(device="cuda").manual_seed(4)
+    dloss = (torch.rand((n,), generator=gen, device="cuda") if reduction == "none"
+             else torch.full((), 0.5, device="cuda"))
+    prior_x = torch.randn((n, h), generator=gen, device="cuda").to(dt) * 1e-6
+    prior_w = [torch.randn((v // p, h), generator=gen, device="cuda").to(dt) * 1e-6 for _ in range(p)]
+    dx = prior_x.clone()
+    dws = [t.clone() for t in prior_w]
+    lce.backward(hidden, shards, targets, lse, dloss, order=order, reduction=reduction, d_hidden=dx, d_shards=dws,
+                 accumulate=acc, grad_dtype=dt)
+    dims = lce.make_dims(n, h, v, p, reduction=reduction, flags=flags)
+    ws = lce.alloc_workspace(n, h, v, p, reduction=reduction, flags=flags)
+    dx_r = prior_x.clone()
+    dws_r = [t.clone() for t in prior_w]
+    for k, s in enumerate(order):
+        lce.bwd_round(dims, k, s, hidden, shards[s], targets, lse, dloss, dx_r, dws_r[s], False, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(dx_r, dx)
+    for a, c in zip(dws_r, dws):
+        assert torch.equal(a, c)
+    # and against the oracle
+    u = dloss.double().cpu().numpy() if reduction == "none" else 0.5
+    ref = oracle.cross_entropy(oracle.bf16_to_f64(b.hidden), oracle.bf16_to_f64(b.weight), b.targets,
+                               reduction=reduction, dloss=u)
+    gx = dx.double().cpu().numpy() - (prior_x.double().cpu().numpy() if acc else 0.0)
+    gw = np.concatenate([(d.double() - (pw.double() if acc else 0.0)).cpu().numpy() for d, pw in zip(dws, prior_w)])
+    e_dx, e_dw = rel_max(gx, ref.d_hidden), rel_max(gw, ref.d_weight)
+    say(f"{variant}: dX rel={e_dx:.2e} dW rel={e_dw:.2e}")
+    assert e_dx <= GRAD_TOL and e_dw <= GRAD_TOL
