@@ -171,6 +171,59 @@ class ClockSampler:
                 "min_mhz": round(v[0], 1), "max_mhz": round(v[-1], 1)}
 
 
+def _time_steps(fn, args, dev):
+    import torch
+    for _ in range(args.warmup):
+        fn()
+    torch.cuda.synchronize(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize(dev)
+    return e0.elapsed_time(e1) / args.steps
+
+
+def variants(lce, hidden, shards, targets, d_hidden, d_shards, dloss, args, out, dev):
+    """The same step through other entry points of the library:
+    * rounds: lce_fwd_round x P, lce_fwd_finish, lce_bwd_round x P, as one rank of
+      a ring calls them (round k holds shard (P - k) mod P);
+    * bf16_grads: lce_forward + lce_backward with bf16 gradient outputs."""
+    import torch
+    n, h = hidden.shape
+    p = len(shards)
+    v = p * shards[0].shape[0]
+    dims = lce.make_dims(n, h, v, p)
+    ws = lce.alloc_workspace(n, h, v, p, dev)
+    order = [(p - k) % p for k in range(p)]
+
+    def rounds():
+        for k, s in enumerate(order):
+            lce.fwd_round(dims, k, s, hidden, shards[s], targets, ws)
+        _, lse = lce.fwd_finish(dims, targets, ws)
+        for k, s in enumerate(order):
+            lce.bwd_round(dims, k, s, hidden, shards[s], targets, lse, dloss, d_hidden, d_shards[s], False, ws)
+
+    ws16 = lce.alloc_workspace(n, h, v, p, dev, flags=lce.FLAG_BF16_GRADS)
+    dx16 = torch.empty((n, h), dtype=torch.bfloat16, device=dev)
+    dw16 = [torch.empty_like(s) for s in shards]
+
+    def bf16_grads():
+        _, lse = lce.forward(hidden, shards, targets, workspace=ws16)
+        lce.backward(hidden, shards, targets, lse, dloss, workspace=ws16, d_hidden=dx16, d_shards=dw16,
+                     grad_dtype=torch.bfloat16)
+
+    res = {}
+    for name, fn in (("rounds", rounds), ("bf16_grads", bf16_grads)):
+        ms = _time_steps(fn, args, dev)
+        res[name] = {"ms_per_step": round(ms, 4), "tokens_per_s": round(n / (ms / 1e3), 1),
+                     "mfma_frac": round(8.0 * n * h * v / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "vs_whole_pass": round(ms / out["ms_per_step"], 4)}
+    del ws, ws16, dx16, dw16
+    return res
+
+
 def materialized(hidden, shards, targets, args, out, dev):
     """The plain path the method replaces, on the same inputs: the full logits
     from a bf16 linear layer, cast to fp32, torch's cross-entropy (mean over
@@ -236,6 +289,9 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--variants", action="store_true",
+                    help="also time the same step through the one-round-at-a-time calls (the ring's per-rank "
+                         "sequence, default ring order) and with bf16 gradient outputs")
     ap.add_argument("--compare-materialized", action="store_true",
                     help="also time the plain materialising path (bf16 linear, fp32 cross-entropy, autograd) on "
                          "the same inputs and report its step time and peak bytes beside this library's")
@@ -416,6 +472,9 @@ def main() -> int:
         "source_sha": kernel_source_sha(),
         "host": platform.node(),
     }
+    if args.variants:
+        print("[bench] timing the per-round and bf16-gradient variants", file=sys.stderr, flush=True)
+        out["variants"] = variants(lce, hidden, shards, targets, d_hidden, d_shards, dloss, args, out, dev)
     if args.compare_materialized:
         print("[bench] timing the materialising path", file=sys.stderr, flush=True)
         out["materialized"] = materialized(hidden, shards, targets, args, out, dev)
