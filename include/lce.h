@@ -31,6 +31,10 @@
  *    positive multiple of 64.
  *  - Limits: N*H, (V/P)*H and N*(V/P) below 2^31 elements; 1 <= P <= 256.
  *  - Calls are thread-safe; concurrent calls need distinct workspaces.
+ *  - An empty batch (N = 0) is valid: the per-token pointers (hidden,
+ *    targets, lse, token_loss, d_hidden, a per-token dloss) may be NULL; the
+ *    loss is NaN for a mean over no tokens and 0 for a sum; the shard
+ *    gradients are zero (left unchanged when accumulating).
  */
 #ifndef LCE_H
 #define LCE_H
@@ -66,7 +70,7 @@ extern "C" {
 #define LCE_MAX_SHARDS 256
 
 typedef struct lce_dims {
-  int64_t n_tokens;     /* N >= 1 */
+  int64_t n_tokens;     /* N >= 0 (an empty batch: see below) */
   int64_t hidden;       /* H >= 64, multiple of 64 */
   int64_t vocab;        /* V >= 1, divisible by n_shards */
   int32_t n_shards;     /* P, 1..LCE_MAX_SHARDS */

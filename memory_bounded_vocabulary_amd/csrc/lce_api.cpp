@@ -69,7 +69,7 @@ struct Plan {
 
 int check_dims(const lce_dims* d) {
   if (!d) return fail(LCE_ERR_INVALID_ARG, "dims is NULL");
-  if (d->n_tokens < 1) return fail(LCE_ERR_INVALID_ARG, "n_tokens must be >= 1 (got %lld)", (long long)d->n_tokens);
+  if (d->n_tokens < 0) return fail(LCE_ERR_INVALID_ARG, "n_tokens must be >= 0 (got %lld)", (long long)d->n_tokens);
   if (d->hidden < 1) return fail(LCE_ERR_INVALID_ARG, "hidden must be >= 1 (got %lld)", (long long)d->hidden);
   if (d->vocab < 1) return fail(LCE_ERR_INVALID_ARG, "vocab must be >= 1 (got %lld)", (long long)d->vocab);
   if (d->n_shards < 1 || d->n_shards > LCE_MAX_SHARDS)
@@ -104,13 +104,13 @@ Plan make_plan(const lce_dims* d) {
   // tile order puts 4 token blocks x 8 splits on an XCD at once), more while
   // the grid would not give every CU a workgroup.
   int64_t s = std::min<int64_t>(
-      {kMaxSplits, p.vocab_tiles, std::max<int64_t>(8, ceil_div(kTargetWorkgroups, p.token_blocks))});
+      {kMaxSplits, p.vocab_tiles, std::max<int64_t>(8, ceil_div(kTargetWorkgroups, std::max<int64_t>(1, p.token_blocks)))});
   p.tiles_per_split = ceil_div(p.vocab_tiles, s);
   p.splits = ceil_div(p.vocab_tiles, p.tiles_per_split);
   // Backward chunks: balanced, tile-aligned, bounded by constants.
   p.vs_pad = round_up(p.Vs, kTile);
   p.vcs = round_up(ceil_div(p.vs_pad, ceil_div(p.vs_pad, kVocabChunkMax)), kTile);
-  p.ncs = round_up(ceil_div(p.n_pad, ceil_div(p.n_pad, kTokenChunkMax)), kTile);
+  p.ncs = p.n_pad ? round_up(ceil_div(p.n_pad, ceil_div(p.n_pad, kTokenChunkMax)), kTile) : 0;
 
   size_t o = 0;
   p.off_state = o;
@@ -169,7 +169,8 @@ int check_common(const lce_dims* d, const void* hidden, const void* const* w_sha
                  void* workspace, size_t workspace_bytes, Plan* plan) {
   int st = check_dims(d);
   if (st) return st;
-  if (!hidden || !w_shards || !targets) return fail(LCE_ERR_INVALID_ARG, "hidden, w_shards and targets must be non-NULL");
+  if (!w_shards || (d->n_tokens > 0 && (!hidden || !targets)))
+    return fail(LCE_ERR_INVALID_ARG, "hidden, w_shards and targets must be non-NULL");
   for (int s = 0; s < d->n_shards; ++s) {
     if (!w_shards[s]) return fail(LCE_ERR_INVALID_ARG, "w_shards[%d] is NULL", s);
     if (!aligned16(w_shards[s])) return fail(LCE_ERR_UNSUPPORTED, "w_shards[%d] is not 16-byte aligned", s);
@@ -427,6 +428,19 @@ int run_bwd_units(const Plan& p, const lce_dims* d, const std::vector<Unit>& uni
   return LCE_OK;
 }
 
+// Empty batch (N = 0): the loss is the mean of no tokens (NaN, as 0/0) or a
+// sum of none (0); a shard gradient is zero.
+int run_empty_loss(const lce_dims* d, float* loss, hipStream_t s) {
+  const float v = d->reduction == LCE_REDUCTION_MEAN ? __builtin_nanf("") : 0.0f;
+  return hip_status(traced(kFinalize, 0.0, 4.0, s, [&] { return lce::launch_set_scalar(loss, v, s); }), "empty loss");
+}
+
+int run_zero(const Plan& p, void* d_w_shard, hipStream_t s) {
+  const size_t bytes = size_t(p.Vs) * p.H * (p.bf16_grads ? 2 : 4);
+  return hip_status(traced(kConvert, 0.0, double(bytes), s, [&] { return lce::launch_zero(d_w_shard, bytes, s); }),
+                    "zero gradient");
+}
+
 int check_round_args(const lce_dims* d, int round, int shard_index, const void* hidden, const void* w_shard,
                      const int32_t* targets, void* workspace, size_t workspace_bytes, Plan* plan) {
   int st = check_dims(d);
@@ -435,7 +449,8 @@ int check_round_args(const lce_dims* d, int round, int shard_index, const void* 
     return fail(LCE_ERR_INVALID_ARG, "round must be in [0, %d) (got %d)", d->n_shards, round);
   if (shard_index < 0 || shard_index >= d->n_shards)
     return fail(LCE_ERR_INVALID_ARG, "shard_index must be in [0, %d) (got %d)", d->n_shards, shard_index);
-  if (!hidden || !w_shard || !targets) return fail(LCE_ERR_INVALID_ARG, "hidden, w_shard and targets must be non-NULL");
+  if (!w_shard || (d->n_tokens > 0 && (!hidden || !targets)))
+    return fail(LCE_ERR_INVALID_ARG, "hidden, w_shard and targets must be non-NULL");
   if (!aligned16(w_shard) || !aligned16(hidden) || !aligned16(targets))
     return fail(LCE_ERR_UNSUPPORTED, "hidden/w_shard/targets not 16-byte aligned");
   *plan = make_plan(d);
@@ -480,8 +495,8 @@ int lce_forward(const lce_dims* d, const void* hidden, const void* const* w_shar
   Plan p;
   int st = check_common(d, hidden, w_shards, targets, workspace, workspace_bytes, &p);
   if (st) return st;
-  if (!loss || !lse) return fail(LCE_ERR_INVALID_ARG, "loss and lse must be non-NULL");
-  if (!token_loss && d->reduction == LCE_REDUCTION_NONE)
+  if (!loss || (d->n_tokens > 0 && !lse)) return fail(LCE_ERR_INVALID_ARG, "loss and lse must be non-NULL");
+  if (d->n_tokens > 0 && !token_loss && d->reduction == LCE_REDUCTION_NONE)
     return fail(LCE_ERR_INVALID_ARG, "token_loss must be non-NULL for LCE_REDUCTION_NONE");
   if (!aligned16(lse) || (token_loss && !aligned16(token_loss)))
     return fail(LCE_ERR_UNSUPPORTED, "lse/token_loss not 16-byte aligned");
@@ -491,6 +506,7 @@ int lce_forward(const lce_dims* d, const void* hidden, const void* const* w_shar
   g_last_error.clear();
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (d->n_tokens == 0) return run_empty_loss(d, loss, s);
   char* ws = static_cast<char*>(workspace);
   lce::ShardTable by_id{}, by_round{};
   for (int k = 0; k < d->n_shards; ++k) {
@@ -518,7 +534,7 @@ int lce_backward(const lce_dims* d, const void* hidden, const void* const* w_sha
   Plan p;
   int st = check_common(d, hidden, w_shards, targets, workspace, workspace_bytes, &p);
   if (st) return st;
-  if (!lse || !dloss || !d_hidden || !d_w_shards)
+  if (!d_w_shards || (d->n_tokens > 0 && (!lse || !dloss || !d_hidden)))
     return fail(LCE_ERR_INVALID_ARG, "lse, dloss, d_hidden and d_w_shards must be non-NULL");
   if (!aligned16(lse) || !aligned16(d_hidden)) return fail(LCE_ERR_UNSUPPORTED, "lse/d_hidden not 16-byte aligned");
   for (int k = 0; k < d->n_shards; ++k) {
@@ -533,6 +549,13 @@ int lce_backward(const lce_dims* d, const void* hidden, const void* const* w_sha
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   const bool acc_dx = (d->flags & LCE_FLAG_ACCUMULATE_DX) != 0, acc_dw = (d->flags & LCE_FLAG_ACCUMULATE_DW) != 0;
+  if (d->n_tokens == 0) {  // no tokens: the shard gradients are zero (or unchanged when accumulating)
+    for (int k = 0; k < d->n_shards && !acc_dw; ++k) {
+      st = run_zero(p, d_w_shards[k], s);
+      if (st) return st;
+    }
+    return LCE_OK;
+  }
   const float* g = nullptr;
   int g_per_token = 0;
   st = run_bwd_scale(p, d, targets, dloss, ws, &g, &g_per_token, s);
@@ -565,6 +588,7 @@ int lce_fwd_round(const lce_dims* d, int round, int shard_index, const void* hid
   by_id.p[shard_index] = static_cast<const uint16_t*>(w_shard);
   by_round.p[0] = static_cast<const uint16_t*>(w_shard);
   const lce::FwdArgs a = fwd_args(p, d, hidden, targets, ws, nullptr, nullptr, nullptr);
+  if (d->n_tokens == 0) return LCE_OK;  // nothing to fold
   st = run_target_logit(p, a, by_id, shard_index, shard_index + 1, round == 0, s);
   if (st) return st;
   return run_fwd_rounds(p, a, by_round, 0, 1, round == 0, 0, s);
@@ -574,9 +598,9 @@ int lce_fwd_finish(const lce_dims* d, const int32_t* targets, float* loss, float
                    void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_dims(d);
   if (st) return st;
-  if (!targets || !loss || !lse || !workspace)
+  if (!loss || !workspace || (d->n_tokens > 0 && (!targets || !lse)))
     return fail(LCE_ERR_INVALID_ARG, "targets, loss, lse and workspace must be non-NULL");
-  if (!token_loss && d->reduction == LCE_REDUCTION_NONE)
+  if (d->n_tokens > 0 && !token_loss && d->reduction == LCE_REDUCTION_NONE)
     return fail(LCE_ERR_INVALID_ARG, "token_loss must be non-NULL for LCE_REDUCTION_NONE");
   if (!aligned16(targets) || !aligned16(lse) || (token_loss && !aligned16(token_loss)) || !aligned16(workspace))
     return fail(LCE_ERR_UNSUPPORTED, "targets/lse/token_loss/workspace not 16-byte aligned");
@@ -584,6 +608,7 @@ int lce_fwd_finish(const lce_dims* d, const int32_t* targets, float* loss, float
   if (workspace_bytes < p.bytes) return fail(LCE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, p.bytes);
   g_last_error.clear();
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (d->n_tokens == 0) return run_empty_loss(d, loss, s);
   const lce::FwdArgs a = fwd_args(p, d, nullptr, targets, static_cast<char*>(workspace), loss, lse, token_loss);
   return hip_status(traced(kFinalize, 0.0, 8.0 * double(p.splits) * double(p.N) + 16.0 * double(p.N), s,
                            [&] { return lce::launch_finalize(a, s); }),
@@ -596,7 +621,7 @@ int lce_bwd_round(const lce_dims* d, int round, int shard_index, const void* hid
   Plan p;
   int st = check_round_args(d, round, shard_index, hidden, w_shard, targets, workspace, workspace_bytes, &p);
   if (st) return st;
-  if (!lse || !dloss || !d_hidden || !d_w_shard)
+  if (!d_w_shard || (d->n_tokens > 0 && (!lse || !dloss || !d_hidden)))
     return fail(LCE_ERR_INVALID_ARG, "lse, dloss, d_hidden and d_w_shard must be non-NULL");
   if (!aligned16(lse) || !aligned16(d_hidden) || !aligned16(d_w_shard))
     return fail(LCE_ERR_UNSUPPORTED, "lse/d_hidden/d_w_shard not 16-byte aligned");
@@ -605,6 +630,7 @@ int lce_bwd_round(const lce_dims* d, int round, int shard_index, const void* hid
   char* ws = static_cast<char*>(workspace);
   const bool acc_dx = round > 0 || (d->flags & LCE_FLAG_ACCUMULATE_DX) != 0;
   const bool acc_dw = accumulate_dw != 0 || (d->flags & LCE_FLAG_ACCUMULATE_DW) != 0;
+  if (d->n_tokens == 0) return acc_dw ? LCE_OK : run_zero(p, d_w_shard, s);
   const float* g = nullptr;
   int g_per_token = 0;
   st = run_bwd_scale(p, d, targets, dloss, ws, &g, &g_per_token, s);

@@ -73,4 +73,8 @@ hipError_t launch_bwd_step(const GradArgs* gr, const BwdGArgs* bg, hipStream_t s
 hipError_t launch_widen_bf16(const uint16_t* src, float* dst, int64_t rows, int64_t cols, hipStream_t st);
 hipError_t launch_narrow_bf16(const float* src, uint16_t* dst, int64_t rows, int64_t cols, hipStream_t st);
 
+// Empty batches: zero `bytes` (a multiple of 16) at p; write one float.
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
+hipError_t launch_set_scalar(float* p, float v, hipStream_t st);
+
 }  // namespace lce

@@ -642,6 +642,15 @@ __global__ __launch_bounds__(256) void narrow_bf16_kernel(const float* __restric
   }
 }
 
+__global__ __launch_bounds__(256) void zero_kernel(u32x4* __restrict__ p, int64_t n16) {
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256) p[i] = z;
+}
+
+__global__ void set_scalar_kernel(float* p, float v) {
+  if (threadIdx.x == 0) *p = v;
+}
+
 // ============================ host launchers ==============================
 static inline hipError_t last() { return hipGetLastError(); }
 
@@ -712,6 +721,18 @@ hipError_t launch_narrow_bf16(const float* src, uint16_t* dst, int64_t rows, int
   const int64_t n8 = rows * cols / 8;
   if (n8 == 0) return hipSuccess;
   hipLaunchKernelGGL(narrow_bf16_kernel, dim3(elementwise_blocks(n8)), dim3(256), 0, st, src, dst, n8);
+  return last();
+}
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t st) {
+  const int64_t n16 = (int64_t)(bytes / 16);
+  if (n16 == 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_kernel, dim3(elementwise_blocks(n16)), dim3(256), 0, st, static_cast<u32x4*>(p), n16);
+  return last();
+}
+
+hipError_t launch_set_scalar(float* p, float v, hipStream_t st) {
+  hipLaunchKernelGGL(set_scalar_kernel, dim3(1), dim3(64), 0, st, p, v);
   return last();
 }
 

@@ -66,7 +66,7 @@ def _bwd(d, hidden=FAKE, lse=FAKE, dloss=FAKE, dx=FAKE, dws=None, ws=FAKE, ws_by
 
 
 @pytest.mark.parametrize("dims,status", [
-    (_dims(n=0), lce.ERR_INVALID_ARG),
+    (_dims(n=-1), lce.ERR_INVALID_ARG),
     (_dims(h=0), lce.ERR_INVALID_ARG),
     (_dims(v=0), lce.ERR_INVALID_ARG),
     (_dims(p=0), lce.ERR_INVALID_ARG),
@@ -271,3 +271,12 @@ def test_plain_c_caller(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stderr
     assert "c abi ok" in r.stdout
+
+
+def test_empty_batch_is_a_valid_shape():
+    d = _dims(n=0)
+    assert lce.lib().lce_workspace_bytes(ctypes.byref(d)) > 0
+    assert lce.state_bytes(d) > 0
+    # per-token pointers may be NULL, the loss and the shard gradients may not
+    assert _fwd(d, loss=None) == lce.ERR_INVALID_ARG
+    assert _bwd(d, dws=[FAKE, None, FAKE, FAKE]) == lce.ERR_INVALID_ARG

@@ -115,3 +115,41 @@ def test_out_of_range_target_gives_nan():
     assert np.all(np.isfinite(np.delete(gpu["token_loss"], 7)))
     assert np.all(np.isnan(gpu["d_hidden"][7])) and np.all(np.isnan(gpu["d_weight"]))
     assert np.all(np.isfinite(np.delete(gpu["d_hidden"], 7, axis=0)))
+
+
+@pytest.mark.parametrize("reduction", ["mean", "sum"])
+def test_empty_batch(reduction):
+    """N = 0: the loss is NaN (mean of nothing) or 0 (sum of nothing); the shard
+    gradients are zero, or unchanged when accumulating; the round calls agree."""
+    import torch
+    import memory_bounded_vocabulary_amd as lce
+    say("empty batch", reduction)
+    h, v, p = 128, 4 * 300, 4
+    gen = torch.Generator(device="cuda").manual_seed(1)
+    shards = [(torch.randn((v // p, h), generator=gen, device="cuda") * 0.05).to(torch.bfloat16) for _ in range(p)]
+    hidden = torch.empty((0, h), dtype=torch.bfloat16, device="cuda")
+    targets = torch.empty((0,), dtype=torch.int32, device="cuda")
+    loss, lse = lce.forward(hidden, shards, targets, reduction=reduction)
+    garbage = [torch.full((v // p, h), 3.0, device="cuda") for _ in range(p)]
+    dx, dws = lce.backward(hidden, shards, targets, lse, 1.0, reduction=reduction,
+                           d_shards=[g.clone() for g in garbage])
+    acc = [g.clone() for g in garbage]
+    lce.backward(hidden, shards, targets, lse, 1.0, reduction=reduction, d_hidden=dx, d_shards=acc, accumulate=True)
+    dims = lce.make_dims(0, h, v, p, reduction=reduction)
+    ws = lce.alloc_workspace(0, h, v, p, reduction=reduction)
+    for k in range(p):
+        lce.fwd_round(dims, k, k, hidden, shards[k], targets, ws)
+    loss_r, _ = lce.fwd_finish(dims, targets, ws)
+    dws_r = [g.clone() for g in garbage]
+    dl = torch.ones((), device="cuda")
+    for k in range(p):
+        lce.bwd_round(dims, k, k, hidden, shards[k], targets, lse, dl, dx, dws_r[k], False, ws)
+    torch.cuda.synchronize()
+    if reduction == "mean":
+        assert math.isnan(loss.item()) and math.isnan(loss_r.item())
+    else:
+        assert loss.item() == 0.0 and loss_r.item() == 0.0
+    assert lse.numel() == 0 and dx.numel() == 0
+    assert all(bool((d == 0).all().item()) for d in dws)
+    assert all(bool((d == 0).all().item()) for d in dws_r)
+    assert all(torch.equal(a, g) for a, g in zip(acc, garbage))
