@@ -136,6 +136,25 @@ def _require_cuda(*tensors) -> None:
             raise ValueError("lce runs on the GPU only: every tensor must be a cuda tensor")
 
 
+def _check_inputs(hidden, shards, targets, lse=None) -> None:
+    """Dtypes, shapes and contiguity the C ABI assumes (it sees raw pointers)."""
+    import torch
+    if hidden.dim() != 2 or hidden.dtype != torch.bfloat16 or not hidden.is_contiguous():
+        raise ValueError("hidden must be a contiguous bf16 [N, H] tensor")
+    if len(shards) < 1:
+        raise ValueError("at least one shard is needed")
+    vs = shards[0].shape[0] if shards[0].dim() == 2 else -1
+    for s in shards:
+        if s.dim() != 2 or s.dtype != torch.bfloat16 or not s.is_contiguous() or tuple(s.shape) != (vs, hidden.shape[1]):
+            raise ValueError("every shard must be a contiguous bf16 [V/P, H] tensor of the same shape")
+    if targets.dim() != 1 or targets.dtype != torch.int32 or not targets.is_contiguous() or \
+            targets.shape[0] != hidden.shape[0]:
+        raise ValueError("targets must be a contiguous int32 [N] tensor")
+    if lse is not None and (lse.dim() != 1 or lse.dtype != torch.float32 or not lse.is_contiguous() or
+                            lse.shape[0] != hidden.shape[0]):
+        raise ValueError("lse must be a contiguous fp32 [N] tensor (from forward)")
+
+
 def state_bytes(dims: Dims) -> int:
     """Leading workspace bytes that carry state between the calls of a round sequence."""
     return int(lib().lce_state_bytes(ctypes.byref(dims)))
@@ -163,6 +182,7 @@ def forward(hidden, shards: Sequence, targets, ignore_index: int = -100, order: 
 
     reduction "none" always returns the token losses (loss is then their sum)."""
     import torch
+    _check_inputs(hidden, shards, targets)
     _require_cuda(hidden, targets, *shards)
     n, h = hidden.shape
     p = len(shards)
@@ -192,6 +212,7 @@ def backward(hidden, shards: Sequence, targets, lse, dloss, ignore_index: int = 
     torch.float32 (default) or torch.bfloat16 (accumulated in fp32, rounded
     once). accumulate: add into the given d_hidden / d_shards."""
     import torch
+    _check_inputs(hidden, shards, targets, lse)
     _require_cuda(hidden, targets, lse, *shards)
     n, h = hidden.shape
     p = len(shards)
@@ -211,6 +232,8 @@ def backward(hidden, shards: Sequence, targets, lse, dloss, ignore_index: int = 
         dloss = torch.tensor(float(dloss), dtype=torch.float32, device=hidden.device)
     if reduction == "none" and dloss.numel() != n:
         raise ValueError("reduction 'none' takes a per-token dloss of N elements")
+    if dloss.dtype != torch.float32 or not dloss.is_contiguous():
+        raise ValueError("dloss must be a contiguous fp32 tensor")
     _require_cuda(dloss)
     if d_hidden is None:
         d_hidden = torch.empty((n, h), dtype=grad_dtype, device=hidden.device)
@@ -219,6 +242,8 @@ def backward(hidden, shards: Sequence, targets, lse, dloss, ignore_index: int = 
     for t in (d_hidden, *d_shards):
         if t.dtype != grad_dtype or not t.is_contiguous():
             raise ValueError(f"gradient buffers must be contiguous {grad_dtype}")
+    if tuple(d_hidden.shape) != (n, h) or len(d_shards) != p or any(tuple(g.shape) != (vs, h) for g in d_shards):
+        raise ValueError("gradient buffers must match hidden [N, H] and the shards [V/P, H]")
     st = lib().lce_backward(ctypes.byref(d), hidden.data_ptr(), _ptr_array([s.data_ptr() for s in shards]),
                             _order_array(order), targets.data_ptr(), lse.data_ptr(), dloss.data_ptr(),
                             d_hidden.data_ptr(), _ptr_array([g.data_ptr() for g in d_shards]),
@@ -229,6 +254,7 @@ def backward(hidden, shards: Sequence, targets, lse, dloss, ignore_index: int = 
 
 def fwd_round(dims: Dims, round_: int, shard_index: int, hidden, shard, targets, workspace, stream=None) -> None:
     """One forward ring round: fold `shard` (id `shard_index`) into the state held in `workspace`."""
+    _check_inputs(hidden, [shard], targets)
     _require_cuda(hidden, shard, targets, workspace)
     _check(lib().lce_fwd_round(ctypes.byref(dims), int(round_), int(shard_index), hidden.data_ptr(),
                                shard.data_ptr(), targets.data_ptr(), workspace.data_ptr(), _nbytes(workspace),
@@ -252,6 +278,10 @@ def fwd_finish(dims: Dims, targets, workspace, token_loss: bool = False, stream=
 def bwd_round(dims: Dims, round_: int, shard_index: int, hidden, shard, targets, lse, dloss, d_hidden, d_shard,
               accumulate_dw: bool, workspace, stream=None) -> None:
     """One backward ring round: d_hidden (+)= G W_shard, d_shard (+)= G^T X for this shard."""
+    _check_inputs(hidden, [shard], targets, lse)
+    for t in (d_hidden, d_shard, dloss, workspace):
+        if not t.is_contiguous():
+            raise ValueError("d_hidden, d_shard, dloss and workspace must be contiguous")
     _require_cuda(hidden, shard, targets, lse, dloss, d_hidden, d_shard, workspace)
     _check(lib().lce_bwd_round(ctypes.byref(dims), int(round_), int(shard_index), hidden.data_ptr(),
                                shard.data_ptr(), targets.data_ptr(), lse.data_ptr(), dloss.data_ptr(),

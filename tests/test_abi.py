@@ -280,3 +280,24 @@ def test_empty_batch_is_a_valid_shape():
     # per-token pointers may be NULL, the loss and the shard gradients may not
     assert _fwd(d, loss=None) == lce.ERR_INVALID_ARG
     assert _bwd(d, dws=[FAKE, None, FAKE, FAKE]) == lce.ERR_INVALID_ARG
+
+
+def test_binding_rejects_layouts_the_abi_cannot_take():
+    """The binding checks dtypes, shapes and contiguity before any pointer reaches
+    the library (host tensors are enough: the checks run before the device check)."""
+    import torch
+    h = torch.zeros((8, 64), dtype=torch.bfloat16)
+    sh = [torch.zeros((16, 64), dtype=torch.bfloat16) for _ in range(2)]
+    t = torch.zeros((8,), dtype=torch.int32)
+    with pytest.raises(ValueError, match="bf16"):
+        lce.forward(h.float(), sh, t)
+    with pytest.raises(ValueError, match="contiguous"):
+        lce.forward(torch.zeros((64, 8), dtype=torch.bfloat16).t(), sh, t)
+    with pytest.raises(ValueError, match="shard"):
+        lce.forward(h, [sh[0], torch.zeros((15, 64), dtype=torch.bfloat16)], t)
+    with pytest.raises(ValueError, match="int32"):
+        lce.forward(h, sh, t.long())
+    with pytest.raises(ValueError, match="lse"):
+        lce.backward(h, sh, t, torch.zeros((7,)), 1.0)
+    with pytest.raises(ValueError, match="GPU"):
+        lce.forward(h, sh, t)
