@@ -83,3 +83,36 @@ def test_full_size_sampled(name):
     assert e_col <= 2.0 ** -5
     assert e_ip <= 1e-3
     assert all(bool(torch.isfinite(d).all().item()) for d in dws) and bool(torch.isfinite(dx).all().item())
+
+
+def test_full_size_rounds_match_whole_pass():
+    """The one-round-at-a-time calls at the large workload's full size (two
+    vocabulary chunks per shard) against the whole-pass calls: the backward bit
+    for bit, the forward's lse within the loss gate."""
+    import torch
+    import memory_bounded_vocabulary_amd as lce
+    w = workloads.WORKLOADS["large"]
+    say("full size rounds", dict(N=w.n_tokens, H=w.hidden, V=w.vocab, P=w.n_shards))
+    b = workloads.make(w)
+    hidden, shards, targets = to_device(b)
+    p = w.n_shards
+    order = [(p - k) % p for k in range(p)]
+    loss, lse = lce.forward(hidden, shards, targets)
+    dx, dws = lce.backward(hidden, shards, targets, lse, torch.ones((), device=hidden.device))
+    dims = lce.make_dims(w.n_tokens, w.hidden, w.vocab, p)
+    ws = lce.alloc_workspace(w.n_tokens, w.hidden, w.vocab, p)
+    for k, s in enumerate(order):
+        lce.fwd_round(dims, k, s, hidden, shards[s], targets, ws)
+    loss_r, lse_r = lce.fwd_finish(dims, targets, ws)
+    dl = torch.ones((), device=hidden.device)
+    dx_r = torch.empty_like(dx)
+    dws_r = [torch.empty_like(d) for d in dws]
+    for k, s in enumerate(order):
+        lce.bwd_round(dims, k, s, hidden, shards[s], targets, lse, dl, dx_r, dws_r[s], False, ws)
+    torch.cuda.synchronize()
+    e = float((lse_r - lse).abs().max().item())
+    say(f"rounds: |dloss|={abs(loss_r.item() - loss.item()):.2e} max|dlse|={e:.2e}")
+    assert abs(loss_r.item() - loss.item()) <= LOSS_TOL
+    assert e <= LOSS_TOL
+    assert torch.equal(dx_r, dx)
+    assert all(torch.equal(a, c) for a, c in zip(dws_r, dws))
