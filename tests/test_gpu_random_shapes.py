@@ -49,3 +49,39 @@ def test_random_shape_parity(case):
     ign_rows = b.targets == -100
     assert np.all(gpu["token_loss"][ign_rows] == 0.0)
     assert np.all(gpu["d_hidden"][ign_rows] == 0.0)
+
+
+RING_CASES = _cases(n_cases=10, seed=77)
+
+
+@pytest.mark.parametrize("case", RING_CASES, ids=[c[0].split(":")[0] for c in RING_CASES])
+def test_random_shape_round_calls(case):
+    """The round calls in a random shard order on random shapes: the backward
+    equals the whole pass bit for bit, the forward within the gate."""
+    import torch
+    import memory_bounded_vocabulary_amd as lce
+    name, n, h, v, p, ign, std, red, order = case
+    order = order or [(p - k) % p for k in range(p)]
+    say("rounds", name, dict(order=order, reduction=red))
+    w = BASE.with_dims(name=name, n_tokens=n, hidden=h, vocab=v, n_shards=p, ignore_frac=ign, w_std=std)
+    b = workloads.make(w, seed=n + 2 * h + v)
+    hidden, shards, targets = to_device(b)
+    loss, lse, tl = lce.forward(hidden, shards, targets, order=order, reduction=red, token_loss=True)
+    dloss = torch.full((), 0.75, device="cuda")
+    dx, dws = lce.backward(hidden, shards, targets, lse, dloss, order=order, reduction=red)
+    dims = lce.make_dims(n, h, v, p, reduction=red)
+    ws = lce.alloc_workspace(n, h, v, p, reduction=red)
+    for k, s in enumerate(order):
+        lce.fwd_round(dims, k, s, hidden, shards[s], targets, ws)
+    loss_r, lse_r, tl_r = lce.fwd_finish(dims, targets, ws, token_loss=True)
+    dx_r = torch.empty_like(dx)
+    dws_r = [torch.empty_like(d) for d in dws]
+    for k, s in enumerate(order):
+        lce.bwd_round(dims, k, s, hidden, shards[s], targets, lse, dloss, dx_r, dws_r[s], False, ws)
+    torch.cuda.synchronize()
+    assert float((lse_r - lse).abs().max().item()) <= 2e-3
+    assert float((tl_r - tl).abs().max().item()) <= 2e-2
+    if np.isfinite(loss.item()):
+        assert abs(loss_r.item() - loss.item()) <= 2e-3 * max(1.0, abs(loss.item()) / 10)
+    assert torch.equal(dx_r, dx)
+    assert all(torch.equal(a, c) for a, c in zip(dws_r, dws))
