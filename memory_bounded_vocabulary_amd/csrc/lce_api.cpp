@@ -4,8 +4,9 @@
 // Schedule (one rank's share of "Flattening Every Memory Peak in Long-Context
 // Mixture-of-Experts Training", section 3.2, Ring-DTP):
 //   forward   target logits; round k = 0..P-1 folds shard order[k] into the
-//             per-token running (m, z); the last round's last arrivals
-//             finalize lse = m + log z, the token losses and the loss.
+//             per-token running (m, z); then a finalize launch merges the
+//             split states into lse = m + log z and the token losses, and a
+//             one-block launch sums the loss.
 //   backward  g = dloss / n_valid; then for every unit (shard in ring order,
 //             vocabulary chunk, token chunk): recompute the logit block from
 //             lse and form G in bf16, then dX += G W_chunk and dW_chunk +=
@@ -59,7 +60,7 @@ struct Plan {
   int64_t splits, tiles_per_split;
   int64_t vs_pad, vcs, ncs;
   // forward workspace
-  size_t off_state, off_yt, off_part, off_counters, fwd_bytes;
+  size_t off_state, off_yt, off_part, fwd_bytes;
   // backward workspace (off_dx32 / off_dw32: fp32 accumulators for bf16 gradients)
   size_t off_gscale, off_g, g_bytes, off_dx32, off_dw32, bwd_bytes;
   size_t state_bytes;  // leading bytes that carry state from one call of a sequence to the next
@@ -118,9 +119,7 @@ Plan make_plan(const lce_dims* d) {
   p.off_yt = o;
   o = align256(o + size_t(p.n_pad) * 4);
   p.off_part = o;
-  o = align256(o + size_t(p.token_blocks) * 16);
-  p.off_counters = o;
-  o = align256(o + size_t(p.token_blocks + 1) * 4);
+  o = align256(o + size_t(std::max<int64_t>(1, p.token_blocks)) * 16);
   p.fwd_bytes = o;
 
   // Backward. What persists between the calls of one sequence sits first
@@ -233,7 +232,6 @@ lce::FwdArgs fwd_args(const Plan& p, const lce_dims* d, const void* hidden, cons
   a.targets = targets;
   a.yt = reinterpret_cast<float*>(ws + p.off_yt);
   a.state = reinterpret_cast<float2*>(ws + p.off_state);
-  a.counters = reinterpret_cast<int*>(ws + p.off_counters);
   a.partials = reinterpret_cast<double2*>(ws + p.off_part);
   a.lse = lse;
   a.token_loss = token_loss;
@@ -259,20 +257,26 @@ int run_target_logit(const Plan& p, const lce::FwdArgs& a, const lce::ShardTable
                            [&] {
                              return lce::launch_target_logit(a.X, a.N, a.H, by_id, a.Vs, int(p.V), s_lo, s_hi,
                                                              a.targets, a.ignore_index, const_cast<float*>(a.yt), init,
-                                                             a.counters, a.token_blocks + 1, s);
+                                                             s);
                            }),
                     "target logits");
 }
 
 int run_fwd_rounds(const Plan& p, const lce::FwdArgs& a, const lce::ShardTable& by_round, int k0, int k1, int first,
-                   int finalize, hipStream_t s) {
+                   hipStream_t s) {
   const double dN = double(p.N), dH = double(p.H), dS = double(p.splits), dVs = double(p.Vs);
   const int nr = k1 - k0;
   const double flops = 2.0 * dN * dVs * dH * nr;
-  const double bytes = 2.0 * dN * dH + 2.0 * dVs * dH * nr + (first ? 8.0 : 16.0) * dS * dN + (finalize ? 16.0 * dN : 0.0);
+  const double bytes = 2.0 * dN * dH + 2.0 * dVs * dH * nr + (first ? 8.0 : 16.0) * dS * dN;
   return hip_status(
-      traced(kFwdRound, flops, bytes, s, [&] { return lce::launch_fwd_rounds(a, by_round, k0, k1, first, finalize, s); }),
+      traced(kFwdRound, flops, bytes, s, [&] { return lce::launch_fwd_rounds(a, by_round, k0, k1, first, s); }),
       "forward rounds");
+}
+
+int run_finalize(const Plan& p, const lce::FwdArgs& a, hipStream_t s) {
+  return hip_status(traced(kFinalize, 0.0, 8.0 * double(p.splits) * double(p.N) + 16.0 * double(p.N), s,
+                           [&] { return lce::launch_finalize(a, s); }),
+                    "finalize");
 }
 
 // One backward unit: a (vocabulary chunk, token chunk) block of one shard.
@@ -522,10 +526,10 @@ int lce_forward(const lce_dims* d, const void* hidden, const void* const* w_shar
   const int per_launch = p.token_blocks * p.splits <= kTargetWorkgroups ? P : 1;
   for (int k = 0; k < P; k += per_launch) {
     const int k1 = std::min(P, k + per_launch);
-    st = run_fwd_rounds(p, a, by_round, k, k1, k == 0, k1 == P, s);
+    st = run_fwd_rounds(p, a, by_round, k, k1, k == 0, s);
     if (st) return st;
   }
-  return LCE_OK;
+  return run_finalize(p, a, s);
 }
 
 int lce_backward(const lce_dims* d, const void* hidden, const void* const* w_shards, const int32_t* shard_order,
@@ -591,7 +595,7 @@ int lce_fwd_round(const lce_dims* d, int round, int shard_index, const void* hid
   if (d->n_tokens == 0) return LCE_OK;  // nothing to fold
   st = run_target_logit(p, a, by_id, shard_index, shard_index + 1, round == 0, s);
   if (st) return st;
-  return run_fwd_rounds(p, a, by_round, 0, 1, round == 0, 0, s);
+  return run_fwd_rounds(p, a, by_round, 0, 1, round == 0, s);
 }
 
 int lce_fwd_finish(const lce_dims* d, const int32_t* targets, float* loss, float* lse, float* token_loss,
@@ -610,9 +614,7 @@ int lce_fwd_finish(const lce_dims* d, const int32_t* targets, float* loss, float
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (d->n_tokens == 0) return run_empty_loss(d, loss, s);
   const lce::FwdArgs a = fwd_args(p, d, nullptr, targets, static_cast<char*>(workspace), loss, lse, token_loss);
-  return hip_status(traced(kFinalize, 0.0, 8.0 * double(p.splits) * double(p.N) + 16.0 * double(p.N), s,
-                           [&] { return lce::launch_finalize(a, s); }),
-                    "finalize");
+  return run_finalize(p, a, s);
 }
 
 int lce_bwd_round(const lce_dims* d, int round, int shard_index, const void* hidden, const void* w_shard,

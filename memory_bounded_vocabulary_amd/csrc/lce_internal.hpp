@@ -15,14 +15,12 @@ struct ShardTable {
 };
 
 // Forward rounds [k_begin, k_end) in one launch (shards.p[k] is the shard met in
-// round k). `first`: no earlier state to merge with. `finalize`: this launch
-// also finalizes (needs target logits of every token already in yt).
+// round k). `first`: no earlier state to merge with.
 struct FwdArgs {
   const uint16_t* X;        // hidden [N][H]
   const int* targets;
   const float* yt;          // target logits from launch_target_logit
   float2* state;            // [S][state_ld] per-split (m, z), log2 domain
-  int* counters;            // token_blocks + 1 arrival counters, zeroed by launch_target_logit
   double2* partials;        // [token_blocks] (loss sum, count)
   float* lse;               // [N]
   float* token_loss;        // [N] or NULL
@@ -30,14 +28,13 @@ struct FwdArgs {
   int N, H, Vs, P, state_ld, token_blocks, S, tiles_per_split, n_vtiles, ignore_index, reduction;
 };
 hipError_t launch_fwd_rounds(const FwdArgs& a, const ShardTable& shards, int k_begin, int k_end, int first,
-                             int finalize, hipStream_t st);
-// Finalize after rounds run one call at a time.
+                             hipStream_t st);
+// After the last round: lse, token losses, block partials, then the loss (two launches).
 hipError_t launch_finalize(const FwdArgs& a, hipStream_t st);
 // Target logits of the tokens whose target lies in shards [s_lo, s_hi)
-// (shards.p indexed by shard id); `init` also resets yt and the counters.
+// (shards.p indexed by shard id); `init` first resets yt.
 hipError_t launch_target_logit(const uint16_t* X, int N, int H, const ShardTable& shards, int Vs, int V, int s_lo,
-                               int s_hi, const int* targets, int ignore_index, float* yt, int init, int* counters,
-                               int n_counters, hipStream_t st);
+                               int s_hi, const int* targets, int ignore_index, float* yt, int init, hipStream_t st);
 hipError_t launch_bwd_scale(const int* targets, int N, int ignore_index, const float* dloss, int reduction,
                             float* gscale, hipStream_t st);
 // Recompute + G of one backward unit (shard, vocabulary chunk, token chunk).

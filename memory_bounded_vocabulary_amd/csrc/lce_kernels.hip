@@ -35,15 +35,8 @@ namespace lce {
 // writer per entry per launch, launches ordered on the stream: no atomics on
 // data). When the grid fits on the CUs at once, one launch covers all rounds;
 // otherwise one launch per round keeps every CU on the same shard, which then
-// stays in the caches.
-//
-// Finalize, fused into the last round: the last of a token block's S
-// workgroups to finish (an atomic arrival counter per block) merges the S
-// states in split order, writes lse = (m + log2 z) ln 2 and the token losses,
-// and a partial sum of the block; the last block to finish sums the partials
-// in block order. All merges run in a fixed order, so the result is bitwise
-// reproducible. The counters are zeroed by target_logit_kernel, which runs
-// first.
+// stays in the caches. The split states are merged by finalize_kernel after
+// the last round's launch.
 // --------------------------------------------------------------------------
 __device__ __forceinline__ void fold_full(const Acc& acc, float (&m)[kNI], float (&z)[kNI]) {
 #pragma unroll
@@ -110,13 +103,9 @@ __device__ __forceinline__ void block_sum256(double& a, long long& b, double* sa
 }
 
 // A workgroup's end: merge the lanes' and waves' (m, z) of its 256 tokens and
-// merge that into state[split][token] (after the earlier rounds'); in the last
-// round, if this is the last of the token block's S splits to arrive, the
-// block's finalize, and if that is the last block, the loss.
+// merge that into state[split][token] (after the earlier rounds').
 __device__ __forceinline__ void fwd_finish_item(const FwdArgs& a, int tb, int split, const float (&m_in)[kNI],
-                                               const float (&z_in)[kNI], int first, int last, char* lds_raw,
-                                               int* s_last_p) {
-  int& s_last = *s_last_p;
+                                               const float (&z_in)[kNI], int first, char* lds_raw) {
   const int wave = wave_id();
   const int lane = lane_id();
   const int wm = wave / kWN, wn = wave % kWN;
@@ -159,62 +148,11 @@ __device__ __forceinline__ void fwd_finish_item(const FwdArgs& a, int tb, int sp
       }
     }
   }
-  if (!last) return;
-
-  // ---- fused finalize: the last split of this token block to arrive ----
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = atomicAdd(&a.counters[tb], 1) == a.S - 1;
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  double* sa = reinterpret_cast<double*>(lds_raw + 4096);
-  long long* sb = reinterpret_cast<long long*>(lds_raw + 8192);
-  double l = 0.0;
-  long long cnt = 0;
-  const int row = tb * kBN + threadIdx.x;
-  if (threadIdx.x < 256 && row < a.N) {
-    float M = kNegBig, Z = 0.0f;
-    for (int s = 0; s < a.S; ++s) {
-      const float2 p = a.state[(size_t)s * a.state_ld + row];
-      lse_merge(M, Z, p.x, p.y);
-    }
-    const float lse = (M + fast_log2(Z)) * kLn2;
-    a.lse[row] = lse;
-    float tl = 0.0f;
-    if (a.targets[row] != a.ignore_index) {
-      tl = lse - a.yt[row];
-      cnt = 1;
-    }
-    if (a.token_loss) a.token_loss[row] = tl;
-    l = tl;
-  }
-  block_sum256(l, cnt, sa, sb);
-  if (threadIdx.x == 0) a.partials[tb] = make_double2(l, (double)cnt);
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = atomicAdd(&a.counters[a.token_blocks], 1) == a.token_blocks - 1;
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  // ---- the last token block: the loss, summing the block partials in order ----
-  double s = 0.0;
-  long long c = 0;
-  if (threadIdx.x < 256) {
-    for (int b = threadIdx.x; b < a.token_blocks; b += 256) {
-      const double2 p = a.partials[b];
-      s += p.x;
-      c += (long long)p.y;
-    }
-  }
-  block_sum256(s, c, sa, sb);
-  if (threadIdx.x == 0) a.loss[0] = (float)(a.reduction == 0 ? s / (double)c : s);
 }
 
 __global__ __launch_bounds__(kThreads, 1) void fwd_round_kernel(FwdArgs a, ShardTable shards, int k_begin,
-                                                                int k_end, int first, int finalize) {
+                                                                int k_end, int first) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[kMainLds];
-  __shared__ int s_last;
   LCE_LDS char* lds = (LCE_LDS char*)lds_raw;
   const int wave = wave_id();
   const int lane = lane_id();
@@ -250,7 +188,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_round_kernel(FwdArgs a, Shard
     else
       fold_masked(acc, m, z, live - lane_row);
   }
-  fwd_finish_item(a, tb, split, m, z, first, finalize, lds_raw, &s_last);
+  fwd_finish_item(a, tb, split, m, z, first, lds_raw);
 }
 
 // --------------------------------------------------------------------------
@@ -258,18 +196,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_round_kernel(FwdArgs a, Shard
 // from the shard that owns t_i, for the tokens whose target lies in the shards
 // [s_lo, s_hi) given (shards.p indexed by shard id). With init, first every
 // ignored token gets 0 and every other token NaN (filled in by this or a later
-// call once its shard is present), and the forward's arrival counters are
-// zeroed: a target outside [0, V) is never filled, so its token's loss, and the
-// mean, stay NaN.
+// call once its shard is present): a target outside [0, V) is never filled, so
+// its token's loss, and the mean, stay NaN.
 // --------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void target_logit_kernel(const uint16_t* __restrict__ X, int N, int H,
                                                            ShardTable shards, int Vs, int V, int s_lo, int s_hi,
                                                            const int* __restrict__ targets, int ignore_index,
-                                                           float* __restrict__ yt, int init,
-                                                           int* __restrict__ counters, int n_counters) {
-  if (init) {  // zero the arrival counters of this forward
-    for (int i = blockIdx.x * 256 + threadIdx.x; i < n_counters; i += gridDim.x * 256) counters[i] = 0;
-  }
+                                                           float* __restrict__ yt, int init) {
   const int lane = lane_id();
   const int row = blockIdx.x * 4 + wave_id();
   if (row >= N) return;
@@ -556,16 +489,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_step_kernel(GradArgs gr, int 
 }
 
 // --------------------------------------------------------------------------
-// Standalone finalize (after rounds run one call at a time): block tb merges
-// the S split states of its 256 tokens in split order, writes lse and the
-// token losses and a partial sum; the last block to finish (arrival counter
-// zeroed by the first round's target_logit_kernel) sums the partials in block
-// order into the loss.
+// Finalize, after the last round's launch: block tb merges the S split states
+// of its 256 tokens in split order, writes lse = (m + log2 z) ln 2 and the
+// token losses, and the block's (loss sum, count) in fixed tree order;
+// loss_kernel then sums the block partials in block order. Two launches, so
+// the only ordering between workgroups is the launch boundary: a device-wide
+// fence inside a launch (an L2 write-back and invalidate on this GPU) cost
+// each workgroup tens of microseconds and evicted its neighbours' operands.
+// Every sum runs in a fixed order, so the result is bitwise reproducible.
 // --------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void finalize_kernel(FwdArgs a) {
   __shared__ double sa[256];
   __shared__ long long sb[256];
-  __shared__ int s_last;
   const int tb = blockIdx.x;
   const int row = tb * 256 + threadIdx.x;
   double l = 0.0;
@@ -588,12 +523,11 @@ __global__ __launch_bounds__(256) void finalize_kernel(FwdArgs a) {
   }
   block_sum256(l, cnt, sa, sb);
   if (threadIdx.x == 0) a.partials[tb] = make_double2(l, (double)cnt);
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = atomicAdd(&a.counters[a.token_blocks], 1) == a.token_blocks - 1;
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+}
+
+__global__ __launch_bounds__(256) void loss_kernel(FwdArgs a) {
+  __shared__ double sa[256];
+  __shared__ long long sb[256];
   double s = 0.0;
   long long c = 0;
   for (int b = threadIdx.x; b < a.token_blocks; b += 256) {
@@ -655,22 +589,24 @@ __global__ void set_scalar_kernel(float* p, float v) {
 static inline hipError_t last() { return hipGetLastError(); }
 
 hipError_t launch_fwd_rounds(const FwdArgs& a, const ShardTable& shards, int k_begin, int k_end, int first,
-                             int finalize, hipStream_t st) {
+                             hipStream_t st) {
   hipLaunchKernelGGL(fwd_round_kernel, dim3(a.token_blocks * a.S), dim3(kThreads), 0, st, a, shards, k_begin, k_end,
-                     first, finalize);
+                     first);
   return last();
 }
 
 hipError_t launch_finalize(const FwdArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(finalize_kernel, dim3(a.token_blocks), dim3(256), 0, st, a);
+  hipError_t e = last();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(loss_kernel, dim3(1), dim3(256), 0, st, a);
   return last();
 }
 
 hipError_t launch_target_logit(const uint16_t* X, int N, int H, const ShardTable& shards, int Vs, int V, int s_lo,
-                               int s_hi, const int* targets, int ignore_index, float* yt, int init, int* counters,
-                               int n_counters, hipStream_t st) {
+                               int s_hi, const int* targets, int ignore_index, float* yt, int init, hipStream_t st) {
   hipLaunchKernelGGL(target_logit_kernel, dim3((N + 3) / 4), dim3(256), 0, st, X, N, H, shards, Vs, V, s_lo, s_hi,
-                     targets, ignore_index, yt, init, counters, n_counters);
+                     targets, ignore_index, yt, init);
   return last();
 }
 
