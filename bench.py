@@ -94,11 +94,19 @@ def cpu_baseline(batch, target_s: float):
                 break
     except OSError:
         pass
-    del np
+    # the forward alone on the same sample, once, for the split (the oracle's
+    # forward forms the same full logit rows without the gradient products)
+    x = oracle.bf16_to_f64(x_all[:n])
+    t0 = time.perf_counter()
+    oracle.cross_entropy(x, wt, batch.targets[:n], grad=False)
+    t_fwd = time.perf_counter() - t0
+    del np, x
     what = f"first {n} of {w.n_tokens} tokens" if n < w.n_tokens else f"all {n} tokens ({reps} passes)"
     return {"value": n * reps / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{what} of the {w.name} batch at full H={w.hidden}, V={w.vocab}, P={w.n_shards}; "
                       f"float64 numpy/BLAS, forward+backward, {t:.1f} s",
+            "forward_tokens_per_s": round(n / t_fwd, 1),
+            "backward_tokens_per_s": round(n / max(t / reps - t_fwd, 1e-9), 1),
             "blas": blas, "cpu": cpu, "affinity_cores": len(os.sched_getaffinity(0))}
 
 
