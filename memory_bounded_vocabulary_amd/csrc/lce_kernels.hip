@@ -356,7 +356,8 @@ __device__ __forceinline__ void recompute_g_tile(const BwdGArgs& a, int id, LCE_
     const int q = it * kThreads + threadIdx.x;
     const int r = q >> 5, c = q & 31;
     const u32x4 v = *reinterpret_cast<const u32x4*>(ldsg + r * 512 + ((c ^ (r & 31)) << 4));
-    *reinterpret_cast<u32x4*>(gt + (size_t)r * a.ldg + c * 8) = v;
+    // non-temporal: G is read back by the next launch, from other XCDs' L2s
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(gt + (size_t)r * a.ldg + c * 8));
   }
 }
 
@@ -401,7 +402,9 @@ __device__ __forceinline__ void rmw_half(float* __restrict__ C, int ldc, int r0,
           v.z += old[k].z;
           v.w += old[k].w;
         }
-        *reinterpret_cast<float4*>(C + (size_t)gr * ldc + gc) = v;
+        // non-temporal: the next add to this tile comes from a later launch
+        const f32x4 nv = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(nv, reinterpret_cast<f32x4*>(C + (size_t)gr * ldc + gc));
       }
     }
   }
