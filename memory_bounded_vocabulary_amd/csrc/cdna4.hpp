@@ -8,7 +8,6 @@ namespace lce {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -23,11 +22,13 @@ constexpr float kNegBig = -3.4028234663852886e38f;
 __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
-// 32x32x16 bf16 MFMA: D = A * B + C. Lane l supplies A[l%32][k-group l/32] and
-// B[k-group l/32][l%32] (8 bf16 each); D element r of lane l sits at
-// row 8*(r/4) + 4*(l/32) + r%4, column l%32.
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+// 16x16x32 bf16 MFMA: D = A * B + C. Lane l supplies A[l%16][8*(l/16) .. +7] and
+// B[8*(l/16) .. +7][l%16] (8 bf16 each); D element e of lane l sits at
+// row 4*(l/16) + e, column l%16. Per flop it draws less power than the
+// 32x32x16 shape, which matters because dense bf16 MFMA work on random data
+// runs this chip into its power limit well below the peak clock.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 // 16-byte global -> LDS copy issued by a whole wave (direct load into LDS):

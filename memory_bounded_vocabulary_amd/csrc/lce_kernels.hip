@@ -19,10 +19,11 @@ namespace lce {
 //
 // The logit tile is computed transposed, W_s rows (vocabulary) x X rows
 // (tokens), so that in the MFMA accumulator layout each lane owns whole token
-// columns: lane l of wave (wm, wn) holds tokens wn*64 + 32 j + l % 32 (j = 0, 1)
-// and, for each, 64 of the tile's 256 vocabulary rows. The online (m, z) of a
-// token (log2 domain) therefore lives in two registers per lane and the fold
-// needs no cross-lane traffic until the end of the round.
+// columns: lane l of wave (wm, wn) holds tokens wn*64 + 16 j + l % 16
+// (j = 0..3) and, for each, 32 of the tile's 256 vocabulary rows. The online
+// (m, z) of a token (log2 domain) therefore lives in two registers per lane
+// and token and the fold needs no cross-lane traffic until the end of the
+// round.
 //
 // A launch covers rounds [k_begin, k_end) (round k meets shards.p[k], the
 // shard a ring would deliver then; the host permutes the table into ring
@@ -45,13 +46,13 @@ __device__ __forceinline__ void fold_full(const Acc& acc, float (&m)[kNI], float
 #pragma unroll
     for (int i = 0; i < kMI; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[i][j][e]);
+      for (int e = 0; e < 4; ++e) mx = fmaxf(mx, acc[i][j][e]);
     const float mn = fmaxf(m[j], mx * kLog2e);
     float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int i = 0; i < kMI; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[e & 3] += fast_exp2(fmaf(acc[i][j][e], kLog2e, -mn));
+      for (int e = 0; e < 4; ++e) s[e] += fast_exp2(fmaf(acc[i][j][e], kLog2e, -mn));
     z[j] = fmaf(z[j], fast_exp2(m[j] - mn), (s[0] + s[1]) + (s[2] + s[3]));
     m[j] = mn;
   }
@@ -62,13 +63,13 @@ __device__ __forceinline__ void fold_full(const Acc& acc, float (&m)[kNI], float
 __device__ __forceinline__ void fold_masked(const Acc& acc, float (&m)[kNI], float (&z)[kNI], int live) {
 #pragma unroll
   for (int j = 0; j < kNI; ++j) {
-    float v[kMI][16];
+    float v[kMI][4];
     float mx = -__builtin_inff();
 #pragma unroll
     for (int i = 0; i < kMI; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int r = 32 * i + 8 * (e >> 2) + (e & 3);
+      for (int e = 0; e < 4; ++e) {
+        const int r = kBlk * i + e;
         v[i][e] = r < live ? acc[i][j][e] : -__builtin_inff();
         mx = fmaxf(mx, v[i][e]);
       }
@@ -77,7 +78,7 @@ __device__ __forceinline__ void fold_masked(const Acc& acc, float (&m)[kNI], flo
 #pragma unroll
     for (int i = 0; i < kMI; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[e & 3] += fast_exp2(fmaf(v[i][e], kLog2e, -mn));
+      for (int e = 0; e < 4; ++e) s[e] += fast_exp2(fmaf(v[i][e], kLog2e, -mn));
     z[j] = fmaf(z[j], fast_exp2(m[j] - mn), (s[0] + s[1]) + (s[2] + s[3]));
     m[j] = mn;
   }
@@ -110,31 +111,35 @@ __device__ __forceinline__ void fwd_finish_item(const FwdArgs& a, int tb, int sp
   const int lane = lane_id();
   const int wm = wave / kWN, wn = wave % kWN;
   float m[kNI], z[kNI];
-  // lanes l and l ^ 32 hold the same tokens (different vocabulary rows)
+  // lanes l, l ^ 16, l ^ 32 and l ^ 48 hold the same tokens (different
+  // vocabulary rows)
 #pragma unroll
   for (int j = 0; j < kNI; ++j) {
     m[j] = m_in[j];
     z[j] = z_in[j];
-    const float m2 = __shfl_xor(m[j], 32);
-    const float z2 = __shfl_xor(z[j], 32);
-    lse_merge(m[j], z[j], m2, z2);
+#pragma unroll
+    for (int x = 16; x <= 32; x *= 2) {
+      const float m2 = __shfl_xor(m[j], x);
+      const float z2 = __shfl_xor(z[j], x);
+      lse_merge(m[j], z[j], m2, z2);
+    }
   }
   // waves wm = 1 hand their tokens' state to waves wm = 0 (LDS is free: the
   // main loop ended on a barrier and no load is in flight)
   __syncthreads();
   float2* red = reinterpret_cast<float2*>(lds_raw);
-  if (wm == 1 && lane < 32) {
+  if (wm == 1 && lane < kBlk) {
 #pragma unroll
-    for (int j = 0; j < kNI; ++j) red[wn * kWaveN + 32 * j + lane] = make_float2(m[j], z[j]);
+    for (int j = 0; j < kNI; ++j) red[wn * kWaveN + kBlk * j + lane] = make_float2(m[j], z[j]);
   }
   __syncthreads();
-  if (wm == 0 && lane < 32) {
+  if (wm == 0 && lane < kBlk) {
 #pragma unroll
     for (int j = 0; j < kNI; ++j) {
-      const float2 o = red[wn * kWaveN + 32 * j + lane];
+      const float2 o = red[wn * kWaveN + kBlk * j + lane];
       float M = m[j], Z = z[j];
       lse_merge(M, Z, o.x, o.y);
-      const int row = tb * kBN + wn * kWaveN + 32 * j + lane;
+      const int row = tb * kBN + wn * kWaveN + kBlk * j + lane;
       if (row < a.N) {
         float2* sp = a.state + (size_t)split * a.state_ld + row;
         if (!first) {  // earlier rounds come first in the merge
@@ -169,7 +174,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_round_kernel(FwdArgs a, Shard
     m[j] = kNegBig;
     z[j] = 0.0f;
   }
-  const int lane_row = wm * kWaveM + 4 * (lane >> 5);  // first vocabulary row of this lane in a tile
+  const int lane_row = wm * kWaveM + 4 * (lane >> 4);  // first vocabulary row of this lane in a tile
   KContigLoader lx, lw;
   lx.init(a.X, a.H, tb * kBN, a.N, wave, lane);
   lw.init(shards.p[k_begin], a.H, t0 * kBM, a.Vs, wave, lane);
@@ -272,7 +277,7 @@ __global__ __launch_bounds__(256) void bwd_scale_kernel(const int* __restrict__ 
 // X and W_s, and its gradient G = g_i (exp(y - lse_i) - [v == t_i]) in bf16
 // (round to nearest even), written to G [token][vocabulary] (row pitch ldg).
 // As in the forward the tile is computed vocabulary x token, so each lane owns
-// two token columns and their (lse, g, target) sit in registers. Rows past the
+// four token columns and their (lse, g, target) sit in registers. Rows past the
 // token chunk (g = 0, lse = +inf) and columns past the vocabulary chunk are
 // written as 0, so G is a dense zero-padded [nc_pad][vc_pad] matrix. The tile
 // is staged in LDS (16-byte chunks of each token row XOR-swizzled by the row)
@@ -298,28 +303,22 @@ __device__ __forceinline__ void recompute_g_tile(const BwdGArgs& a, int id, LCE_
   int tt, tv;
   xcd_tile(id, a.n_tt, a.n_tv, tt, tv);
 
-  // per-lane token info: log2-domain lse, gradient scale, target row in this tile
-  float lse2[kNI], g[kNI];
-  int tcol[kNI];
+  // per-lane token info, loaded before the main loop (unconditionally, from a
+  // clamped row, so that the loads complete under the loop's first wait) and
+  // turned into (log2-domain lse, gradient scale, target row in this tile)
+  // after it
+  float lse_raw[kNI], gs_raw[kNI];
+  int t_raw[kNI];
+  bool valid[kNI];
 #pragma unroll
   for (int j = 0; j < kNI; ++j) {
-    const int rr = tt * kBN + wn * kWaveN + 32 * j + (lane & 31);
+    const int rr = tt * kBN + wn * kWaveN + kBlk * j + (lane & 15);
     const int row = a.n0 + rr;
-    lse2[j] = __builtin_inff();
-    g[j] = 0.0f;
-    tcol[j] = -1;
-    if (rr < a.nc && row < a.N) {
-      lse2[j] = a.lse[row] * kLog2e;
-      const int t = a.targets[row];
-      if (t != a.ignore_index) {
-        if (t < 0 || t >= a.V) {
-          g[j] = __builtin_nanf("");
-        } else {
-          g[j] = a.gscale[a.g_per_token ? row : 0];
-          tcol[j] = t - (a.vocab_base + tv * kBM);
-        }
-      }
-    }
+    valid[j] = rr < a.nc && row < a.N;
+    const int rc = valid[j] ? row : a.n0;  // a.n0 < a.N: the tile exists
+    lse_raw[j] = a.lse[rc];
+    t_raw[j] = a.targets[rc];
+    gs_raw[j] = a.gscale[a.g_per_token ? rc : 0];
   }
   KContigLoader lw, lx;
   lw.init(a.Ws, a.H, a.v0 + tv * kBM, a.Vs, wave, lane);
@@ -327,27 +326,45 @@ __device__ __forceinline__ void recompute_g_tile(const BwdGArgs& a, int id, LCE_
   Acc acc;
   tile_mainloop<false, false>(lw, lx, a.H, lds, acc);
 
+  float lse2[kNI], g[kNI];
+  int tcol[kNI];
+#pragma unroll
+  for (int j = 0; j < kNI; ++j) {
+    lse2[j] = __builtin_inff();
+    g[j] = 0.0f;
+    tcol[j] = -1;
+    if (valid[j]) {
+      lse2[j] = lse_raw[j] * kLog2e;
+      const int t = t_raw[j];
+      if (t != a.ignore_index) {
+        if (t < 0 || t >= a.V) {
+          g[j] = __builtin_nanf("");
+        } else {
+          g[j] = gs_raw[j];
+          tcol[j] = t - (a.vocab_base + tv * kBM);
+        }
+      }
+    }
+  }
   const int live = a.vc - tv * kBM;  // vocabulary rows of this tile inside the chunk
 #pragma unroll
   for (int j = 0; j < kNI; ++j) {
-    const int tok = wn * kWaveN + 32 * j + (lane & 31);  // token row of the staged tile
+    const int tok = wn * kWaveN + kBlk * j + (lane & 15);  // token row of the staged tile
 #pragma unroll
-    for (int i = 0; i < kMI; ++i)
+    for (int i = 0; i < kMI; ++i) {
+      const int r0 = wm * kWaveM + kBlk * i + 4 * (lane >> 4);  // 4 consecutive vocabulary rows
+      float gv[4];
 #pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const int r0 = wm * kWaveM + 32 * i + 8 * e4 + 4 * (lane >> 5);  // 4 consecutive vocabulary rows
-        float gv[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int r = r0 + q;
-          const float p = fast_exp2(fmaf(acc[i][j][4 * e4 + q], kLog2e, -lse2[j]));
-          const float v = g[j] * (p - (r == tcol[j] ? 1.0f : 0.0f));
-          gv[q] = r < live ? v : 0.0f;
-        }
-        const int slot = (r0 >> 3) ^ (tok & 31);
-        uint2 packed = make_uint2(pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3]));
-        *reinterpret_cast<uint2*>(ldsg + tok * 512 + slot * 16 + (r0 & 7) * 2) = packed;
+      for (int q = 0; q < 4; ++q) {
+        const int r = r0 + q;
+        const float p = fast_exp2(fmaf(acc[i][j][q], kLog2e, -lse2[j]));
+        const float v = g[j] * (p - (r == tcol[j] ? 1.0f : 0.0f));
+        gv[q] = r < live ? v : 0.0f;
       }
+      const int slot = (r0 >> 3) ^ (tok & 31);
+      uint2 packed = make_uint2(pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3]));
+      *reinterpret_cast<uint2*>(ldsg + tok * 512 + slot * 16 + (r0 & 7) * 2) = packed;
+    }
   }
   __syncthreads();
   uint16_t* gt = a.G + (size_t)tt * kBN * a.ldg + (size_t)tv * kBM;
@@ -367,9 +384,10 @@ __device__ __forceinline__ void recompute_g_tile(const BwdGArgs& a, int id, LCE_
 // waves with wm = 0, then wm = 1), so that global memory sees 16-byte accesses
 // along whole rows, and all of a thread's loads of C are issued before the
 // first of them is waited for. LDS row r holds the 256 floats of the row, with
-// the two 128-byte column halves swapped on rows where (r >> 2) is odd, so the
-// two 32-lane halves of an accumulator write (rows r and r + 4) use different
-// banks. Needs the 128 KB of LDS free (the main loop ends on a barrier).
+// column c stored at c ^ (16 ((r >> 2) & 3)), so the four 16-lane groups of an
+// accumulator write (rows r, r + 4, r + 8, r + 12, 16 columns each) use
+// different banks. Needs the 128 KB of LDS free (the main loop ends on a
+// barrier).
 // kIt 16-byte chunks of one 128-row half, in batches of kBatch: a batch's
 // loads of C are all issued before the first is waited for.
 template <int kIt, bool kFull, bool kAcc>
@@ -395,7 +413,7 @@ __device__ __forceinline__ void rmw_half(float* __restrict__ C, int ldc, int r0,
       const int r = (b0 + k) * (kThreads / 64) + (threadIdx.x >> 6);
       const int gr = r0 + r;
       if (kFull || (gr < m_valid && gc < n_valid)) {
-        float4 v = *reinterpret_cast<const float4*>(tile + r * 256 + 4 * (c ^ (8 * ((r >> 2) & 1))));
+        float4 v = *reinterpret_cast<const float4*>(tile + r * 256 + 4 * (c ^ (4 * ((r >> 2) & 3))));
         if (kAcc) {
           v.x += old[k].x;
           v.y += old[k].y;
@@ -423,12 +441,12 @@ __device__ __forceinline__ void store_tile(const Acc& acc, float* __restrict__ C
 #pragma unroll
       for (int i = 0; i < kMI; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int r = 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        for (int e = 0; e < 4; ++e) {
+          const int r = kBlk * i + 4 * (lane >> 4) + e;
 #pragma unroll
           for (int j = 0; j < kNI; ++j) {
-            const int c = wn * kWaveN + 32 * j + (lane & 31);
-            tile[r * 256 + (c ^ (32 * ((r >> 2) & 1)))] = acc[i][j][e];
+            const int c = wn * kWaveN + kBlk * j + (lane & 15);
+            tile[r * 256 + (c ^ (16 * ((r >> 2) & 3)))] = acc[i][j][e];
           }
         }
     }

@@ -11,14 +11,17 @@
 // they are, and the fragment reads transpose them (ds_read_tr16_b64).
 //
 // Workgroup: 512 threads = 8 waves, two per SIMD, arranged 2 (M) x 4 (N); each
-// wave owns a 128 x 64 sub-tile held as 4 x 2 accumulators of the 32x32x16 bf16
+// wave owns a 128 x 64 sub-tile held as 8 x 4 accumulators of the 16x16x32 bf16
 // MFMA (128 fp32 per lane). Two waves per SIMD let one wave's LDS traffic and
-// waits hide under the other's MFMAs.
+// waits hide under the other's MFMAs. The 16x16x32 shape does the same work
+// per LDS byte as 32x32x16 here but draws less power per flop, and this chip
+// reaches its power limit before its peak clock on dense bf16 work.
 //
-// K advances 64 per stage through two LDS stages (A and B, 32 KB each, 128 KB
-// total) filled by direct global->LDS 16-byte loads. Within a stage, the
-// fragments of k-step s+1 are read from LDS while the MFMAs of k-step s run;
-// the loads of the next stage are in flight during the whole stage.
+// K advances 64 per stage (two k-steps of 32) through two LDS stages (A and B,
+// 32 KB each, 128 KB total) filled by direct global->LDS 16-byte loads. The
+// fragments of k-step 1 are read from LDS while the MFMAs of k-step 0 run, and
+// those of the next stage's k-step 0 while the MFMAs of k-step 1 run; the
+// loads of the next stage are in flight during the whole stage.
 //
 // LDS layouts (one operand, one stage, 32 KB):
 //  K-contiguous: 256 rows x 128 bytes (64 bf16 of K), as 16-byte chunks; chunk
@@ -44,10 +47,12 @@ constexpr int kMainLds = 2 * kStageBytes;    // double-buffered: 128 KB
 constexpr int kWM = 2, kWN = 4;              // wave grid over the tile
 constexpr int kWaveM = kBM / kWM;            // 128
 constexpr int kWaveN = kBN / kWN;            // 64
-constexpr int kMI = kWaveM / 32;             // 4 accumulator rows of blocks
-constexpr int kNI = kWaveN / 32;             // 2 accumulator columns of blocks
+constexpr int kBlk = 16;                     // MFMA block edge
+constexpr int kKStep = 32;                   // K per MFMA
+constexpr int kMI = kWaveM / kBlk;           // 8 accumulator rows of blocks
+constexpr int kNI = kWaveN / kBlk;           // 4 accumulator columns of blocks
 
-typedef f32x16 Acc[kMI][kNI];
+typedef f32x4 Acc[kMI][kNI];
 
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int kmaj_swz(int k) { return (2 * (k & 3)) ^ (8 * (k & 1)); }
@@ -58,35 +63,45 @@ __device__ __forceinline__ int kmaj_swz(int k) { return (2 * (k & 3)) ^ (8 * (k 
 // K-contiguous operand: tile rows row0..row0+255 of a [rows][ld] bf16 matrix.
 // Rows at or past rows_valid are clamped to the last valid row: they load real
 // (finite) data whose results the epilogues discard or whose partner operand
-// is zero there.
+// is zero there. Load j of a wave fills tile rows 32 wave + 8 j + lane / 8; the
+// per-lane state is two registers, and each load's address is formed when it
+// is issued (a few VALU per 16-byte load), which keeps the main loop's
+// register footprint small.
 struct KContigLoader {
   const char* base;
-  uint32_t off[4];
+  uint32_t ld2;   // row pitch in bytes
+  int row;        // this lane's row for load 0 (absolute)
+  int last;       // last valid row
+  uint32_t kc16;  // byte offset of this lane's chunk for even j (odd j: ^ 16)
 
   __device__ __forceinline__ void init(const uint16_t* p, int ld, int row0, int rows_valid, int wave, int lane) {
     base = reinterpret_cast<const char*>(p);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = wave * 32 + j * 8 + (lane >> 3);
-      const int kc = (lane & 7) ^ swz(r);
-      const int gr = min(row0 + r, rows_valid - 1);
-      off[j] = (uint32_t)gr * (uint32_t)ld * 2u + (uint32_t)kc * 16u;
-    }
+    ld2 = (uint32_t)ld * 2u;
+    row = row0 + wave * 32 + (lane >> 3);
+    last = rows_valid - 1;
+    // chunk (lane & 7) of row r sits in slot (lane & 7) ^ swz(r); for these rows
+    // swz(r) = (lane >> 3) ^ (j & 1)
+    kc16 = (uint32_t)(((lane & 7) ^ (lane >> 3)) * 16);
   }
   __device__ __forceinline__ void issue(int k0, LCE_LDS char* tile, int wave) const {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) g2lds16(base, off[j] + (uint32_t)k0 * 2u, tile + (wave * 4 + j) * 1024);
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t gr = (uint32_t)min(row + 8 * j, last);
+      g2lds16(base, gr * ld2 + (kc16 ^ (16u * (j & 1))) + (uint32_t)k0 * 2u, tile + (wave * 4 + j) * 1024);
+    }
   }
 };
 
 // K-major operand: element (m, k) at p[k * ld + m]; the tile covers columns
 // m0..m0+255 and rows k0..k0+63. Columns past m_valid (a multiple of 8) and
-// rows past k_valid are clamped to the last valid ones.
+// rows past k_valid are clamped to the last valid ones. Load j of a wave fills
+// tile rows 8 wave + 2 j and 8 wave + 2 j + 1 (lanes 0-31 and 32-63), 16 bytes
+// per lane.
 struct KMajorLoader {
   const char* base;
   uint32_t ld2;       // row pitch in bytes
-  uint32_t col[4];    // byte offset of this lane's 16-byte chunk within a row
-  int row[4];         // tile row (k) this lane fills, per load
+  uint32_t col[2];    // byte offset of this lane's chunk within a row, for even / odd j
+  int row;            // tile row (k) this lane fills for load 0
   int k_last;
 
   __device__ __forceinline__ void init(const uint16_t* p, int ld, int m0, int m_valid, int k_valid, int wave,
@@ -94,70 +109,81 @@ struct KMajorLoader {
     base = reinterpret_cast<const char*>(p);
     ld2 = (uint32_t)ld * 2u;
     k_last = k_valid - 1;
+    row = 8 * wave + (lane >> 5);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int q = wave * 4 + j;           // 1 KB piece = tile rows 2q, 2q+1
-      const int r = 2 * q + (lane >> 5);
+    for (int h = 0; h < 2; ++h) {
+      const int r = row + 2 * h;             // kmaj_swz depends on r & 3 only
       const int c = (lane & 31) ^ kmaj_swz(r);
-      const int m = min(m0 + c * 8, m_valid - 8);
-      row[j] = r;
-      col[j] = (uint32_t)m * 2u;
+      col[h] = (uint32_t)min(m0 + c * 8, m_valid - 8) * 2u;
     }
   }
   __device__ __forceinline__ void issue(int k0, LCE_LDS char* tile, int wave) const {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t kr = (uint32_t)min(k0 + row[j], k_last);
-      g2lds16(base, kr * ld2 + col[j], tile + (wave * 4 + j) * 1024);
+      const uint32_t kr = (uint32_t)min(k0 + row + 2 * j, k_last);
+      g2lds16(base, kr * ld2 + col[j & 1], tile + (wave * 4 + j) * 1024);
     }
   }
 };
 
 // ---- LDS -> register fragments --------------------------------------------
-// Fragment of block i (32 rows of the wave's sub-tile) for k-step ks: lane l
-// holds operand row (l % 32) and k = 16 ks + 8 (l / 32) + 0..7.
+// Fragment of block i (16 rows of the wave's sub-tile) for k-step ks: lane l
+// holds operand row (l % 16) and k = 32 ks + 8 (l / 16) + 0..7.
 
 template <int NB>
 struct KContigReader {
   int base;  // byte offset of this lane's row in the operand tile
   int sw;
   __device__ __forceinline__ void init(int wrow, int lane) {
-    base = (wrow + (lane & 31)) * 128;
-    sw = swz(lane & 31);
+    base = (wrow + (lane & 15)) * 128;
+    sw = swz(lane & 15);  // wrow + 16 i adds nothing to the low four row bits
   }
   __device__ __forceinline__ void read(const LCE_LDS char* tile, int ks, int lane, bf16x8 (&f)[NB]) const {
-    const int slot = ((ks * 2 + (lane >> 5)) ^ sw) * 16;
+    read_range<0, NB>(tile, ks, lane, f);
+  }
+  // fragments [I0, I1) into f[0 .. I1 - I0) (f may be shorter than NB)
+  template <int I0, int I1, int NF>
+  __device__ __forceinline__ void read_range(const LCE_LDS char* tile, int ks, int lane, bf16x8 (&f)[NF]) const {
+    static_assert(I1 - I0 <= NF && I1 <= NB, "fragment range");
+    const int slot = ((ks * 4 + (lane >> 4)) ^ sw) * 16;
 #pragma unroll
-    for (int i = 0; i < NB; ++i) f[i] = *reinterpret_cast<const LCE_LDS bf16x8*>(tile + base + i * 4096 + slot);
+    for (int i = I0; i < I1; ++i)
+      f[i - I0] = *reinterpret_cast<const LCE_LDS bf16x8*>(tile + base + i * kBlk * 128 + slot);
   }
 };
 
 // Transposing read of a K-major tile. ds_read_tr16_b64 works on groups of 16
 // lanes: each lane loads 4 consecutive bf16 and lane i of the group receives
 // element (i % 4) of lanes 4q + i / 4, q = 0..3. A lane at position 4q + r of
-// its group therefore loads row k = kbase + q, columns mbase + 4r .. +3, so
-// that lane i receives column mbase + i at rows kbase .. kbase + 3; two such
-// reads (k + 0..3, k + 4..7) make one 8-element fragment.
+// group g = l / 16 therefore loads row k = 8 g + q, columns mbase + 4r .. +3, so
+// that lane i of the group receives column mbase + i at rows 8 g .. 8 g + 3; two
+// such reads (rows + 0..3, + 4..7) make the 8-element fragment of k-group g.
 template <int NB>
 struct KMajorReader {
   int off[NB];  // byte offset for k-step 0, first half
   __device__ __forceinline__ void init(int wrow, int lane) {
     const int q = (lane & 15) >> 2, r = lane & 3;
-    const int k = 8 * (lane >> 5) + q;
+    const int k = 8 * (lane >> 4) + q;
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      const int m = wrow + 32 * i + 16 * ((lane >> 4) & 1) + 4 * r;
+      const int m = wrow + kBlk * i + 4 * r;
       off[i] = k * 512 + (((m >> 3) ^ kmaj_swz(k)) << 4) + (m & 7) * 2;
     }
   }
   __device__ __forceinline__ void read(const LCE_LDS char* tile, int ks, int lane, bf16x8 (&f)[NB]) const {
+    read_range<0, NB>(tile, ks, lane, f);
+  }
+  // fragments [I0, I1) into f[0 .. I1 - I0) (f may be shorter than NB)
+  template <int I0, int I1, int NF>
+  __device__ __forceinline__ void read_range(const LCE_LDS char* tile, int ks, int lane, bf16x8 (&f)[NF]) const {
+    static_assert(I1 - I0 <= NF && I1 <= NB, "fragment range");
     (void)lane;
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      // rows k and k + 4 have the same (k & 3), so the same swizzle
-      const bf16x4 lo = ds_read_tr16(tile + off[i] + ks * 16 * 512);
-      const bf16x4 hi = ds_read_tr16(tile + off[i] + ks * 16 * 512 + 4 * 512);
-      f[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    for (int i = I0; i < I1; ++i) {
+      // rows k, k + 4 and k + 32 ks have the same (k & 3), so the same swizzle
+      const bf16x4 lo = ds_read_tr16(tile + off[i] + ks * kKStep * 512);
+      const bf16x4 hi = ds_read_tr16(tile + off[i] + ks * kKStep * 512 + 4 * 512);
+      f[i - I0] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
   }
 };
@@ -176,81 +202,75 @@ __device__ __forceinline__ void mma_step(Acc& acc, const bf16x8 (&a)[MI], const 
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < NI; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+    for (int j = 0; j < NI; ++j) acc[i][j] = mfma16(a[i], b[j], acc[i][j]);
 }
 
-// Ask the scheduler to put one LDS read after each of the first n MFMAs of the
-// step, then the remaining MFMAs.
-// Ask the scheduler to spread NVM global->LDS loads and NDS LDS reads evenly
-// over the NMFMA MFMAs of a k-step (masks: 0x008 MFMA, 0x020 global load,
-// 0x100 LDS read).
-template <int I, int NMFMA, int NVM, int NDS>
+// Ask the scheduler for the order of one k-step (masks: 0x008 MFMA, 0x100 LDS
+// read): after MFMA t, X(t) of the next k-step's fragment reads, where the
+// reads are issued in source order. mma_step runs j fastest, so MFMA 4 i + 3
+// is the last one that uses A fragment i; a read that refills A fragment i
+// must not be issued before it, or its register could not be reused.
+//  kSteady: the B reads (NB) one per MFMA from the start, then the AR reads of
+//    A fragment i after MFMA 4 i + 3. Source order: B, then A by block.
+//  !kSteady (before a barrier): the same, but the reads of A fragments 6 and 7
+//    go into spare registers right after the B reads, so that the last refill
+//    (fragment 5) follows MFMA 23 and its latency is hidden before the barrier
+//    at the end of the k-step. Source order: B, A6, A7, then A0 .. A5.
+// In both cases each read lands at or after its planned MFMA, never before.
+template <int I, int NMFMA, int NB, int AR, bool kSteady>
 __device__ __forceinline__ void interleave_from() {
   if constexpr (I < NMFMA) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    constexpr int nv = NVM / NMFMA + (I < NVM % NMFMA ? 1 : 0);
-    constexpr int nd = NDS / NMFMA + (I < NDS % NMFMA ? 1 : 0);
-    if constexpr (nv > 0) __builtin_amdgcn_sched_group_barrier(0x020, nv, 0);
+    constexpr int early = kSteady ? NB : NB + 2 * AR;
+    constexpr int last_refill = kSteady ? kMI - 1 : kMI - 3;
+    constexpr int nd = (I < early ? 1 : 0) + (I % kNI == kNI - 1 && I / kNI <= last_refill ? AR : 0);
     if constexpr (nd > 0) __builtin_amdgcn_sched_group_barrier(0x100, nd, 0);
-    interleave_from<I + 1, NMFMA, NVM, NDS>();
+    interleave_from<I + 1, NMFMA, NB, AR, kSteady>();
   }
 }
-template <int NMFMA, int NDS>
-__device__ __forceinline__ void interleave_mfma_ds() {
-  interleave_from<0, NMFMA, 0, NDS>();
-}
-template <int NMFMA, int NVM, int NDS>
-__device__ __forceinline__ void interleave_mfma_vmem_ds() {
-  interleave_from<0, NMFMA, NVM, NDS>();
-}
 
-// One stage (64 of K) of the main loop, branch-free so the scheduling
-// barriers can interleave across the whole body. On entry the fragments of
-// k-step 0 of this stage are in (a0, b0) and the stage's tiles are in LDS
-// buffer kt & 1; the next stage's tiles are in flight into the other buffer.
-// k-steps 0..2: read the next k-step's fragments while the MFMAs of the
-// current one run. Then wait for the next stage's tiles and pass a barrier
-// (after which no wave reads this stage's buffer again), and during k-step 3
-// issue the loads of stage kt + 2 into this stage's buffer (kIssue) and read
-// k-step 0 of the next stage (kNext).
-template <bool A_KMAJ, bool B_KMAJ, bool kIssue, bool kNext, class LA, class LB, class RA, class RB>
-__device__ __forceinline__ void mainloop_stage(int kt, const LA& la, const LB& lb, const RA& ra, const RB& rb,
-                                               LCE_LDS char* lds, int wave, int lane, Acc& acc, bf16x8 (&a0)[kMI],
-                                               bf16x8 (&b0)[kNI], bf16x8 (&a1)[kMI], bf16x8 (&b1)[kNI]) {
-  constexpr int kReads = (A_KMAJ ? 2 : 1) * kMI + (B_KMAJ ? 2 : 1) * kNI;
-  constexpr int kLoads = 8;  // global->LDS loads per wave per stage
+// One stage (64 of K) of the main loop. On entry the fragments of k-step 0 of
+// this stage are in (a, b0) and the stage's tiles are in LDS buffer kt & 1;
+// the next stage's tiles are in flight into the other buffer. k-step 0: read
+// k-step 1's fragments into (a, b1) while its MFMAs run (fragments 6 and 7 of
+// A via a6, a7). Then wait for the next stage's tiles and pass a barrier
+// (after which no wave reads this stage's buffer again), issue the loads of
+// stage kt + 2 into this stage's buffer (if there is one), and during k-step 1
+// read k-step 0 of the next stage into (a, b0). The last stage reads the other
+// buffer too, whatever it holds then (the values are never used): keeping
+// those reads unconditional keeps them in the same basic block as the MFMAs
+// they interleave with.
+template <bool A_KMAJ, bool B_KMAJ, class LA, class LB, class RA, class RB>
+__device__ __forceinline__ void mainloop_stage(int kt, int kt_n, const LA& la, const LB& lb, const RA& ra,
+                                               const RB& rb, LCE_LDS char* lds, int wave, int lane, Acc& acc,
+                                               bf16x8 (&a)[kMI], bf16x8 (&b0)[kNI], bf16x8 (&b1)[kNI]) {
+  constexpr int kAR = A_KMAJ ? 2 : 1;            // LDS reads per A fragment
+  constexpr int kBR = (B_KMAJ ? 2 : 1) * kNI;    // LDS reads of the B fragments
   LCE_LDS char* cur = lds + (kt & 1) * kStageBytes;
   LCE_LDS char* nxt = lds + ((kt + 1) & 1) * kStageBytes;
-  ra.read(cur, 1, lane, a1);
+  static_assert(kBK == 2 * kKStep, "two k-steps per stage");
+  static_assert(kMI == 8 && kNI == 4, "read schedule written for 8 x 4 blocks");
+  mma_step<kMI, kNI>(acc, a, b0);
   rb.read(cur + kOpBytes, 1, lane, b1);
-  mma_step<kMI, kNI>(acc, a0, b0);
-  interleave_mfma_ds<kMI * kNI, kReads>();
-  ra.read(cur, 2, lane, a0);
-  rb.read(cur + kOpBytes, 2, lane, b0);
-  mma_step<kMI, kNI>(acc, a1, b1);
-  interleave_mfma_ds<kMI * kNI, kReads>();
-  ra.read(cur, 3, lane, a1);
-  rb.read(cur + kOpBytes, 3, lane, b1);
-  mma_step<kMI, kNI>(acc, a0, b0);
-  interleave_mfma_ds<kMI * kNI, kReads>();
+  bf16x8 a67[2];
+  ra.template read_range<6, 8>(cur, 1, lane, a67);
+  ra.template read_range<0, 6>(cur, 1, lane, a);
+  interleave_from<0, kMI * kNI, kBR, kAR, false>();
+  __builtin_amdgcn_sched_barrier(0);  // all of k-step 0 before the barrier
+  a[6] = a67[0];
+  a[7] = a67[1];
   wait_vm0();
   wait_lgkm0();
   __syncthreads();
   __builtin_amdgcn_sched_barrier(0);
-  if (kIssue) {
+  if (kt + 2 < kt_n) {
     la.issue((kt + 2) * kBK, cur, wave);
     lb.issue((kt + 2) * kBK, cur + kOpBytes, wave);
   }
-  if (kNext) {
-    ra.read(nxt, 0, lane, a0);
-    rb.read(nxt + kOpBytes, 0, lane, b0);
-  }
-  mma_step<kMI, kNI>(acc, a1, b1);
-  if (kIssue && kNext) {
-    interleave_mfma_vmem_ds<kMI * kNI, kLoads, kReads>();
-  } else if (kNext) {
-    interleave_mfma_ds<kMI * kNI, kReads>();
-  }
+  mma_step<kMI, kNI>(acc, a, b1);
+  rb.read(nxt + kOpBytes, 0, lane, b0);
+  ra.read(nxt, 0, lane, a);
+  interleave_from<0, kMI * kNI, kBR, kAR, true>();
 }
 
 // Issues the loads of the first two stages of a tile (one if K = 64). A caller
@@ -271,8 +291,10 @@ __device__ __forceinline__ void tile_prologue(const LA& la, const LB& lb, int K,
 // Full K loop for one tile (K a positive multiple of 64). The accumulators are
 // zeroed here. With kIssued the first stages were issued by tile_prologue and
 // the wave has issued no other memory operation since. On return every wave
-// has passed a barrier after its last LDS read and no load into LDS is in
-// flight, so both LDS stages are free for the caller.
+// has passed a barrier after its last LDS read whose value is used, and no
+// load into LDS is in flight, so both LDS stages are free for the caller (the
+// discarded reads of the last stage may still be in flight: they read, never
+// write, and nothing uses what they return).
 template <bool A_KMAJ, bool B_KMAJ, bool kIssued = false, class LA, class LB>
 __device__ __forceinline__ void tile_mainloop(const LA& la, const LB& lb, int K, LCE_LDS char* lds, Acc& acc) {
   const int wave = wave_id();
@@ -285,7 +307,7 @@ __device__ __forceinline__ void tile_mainloop(const LA& la, const LB& lb, int K,
 #pragma unroll
   for (int i = 0; i < kMI; ++i)
 #pragma unroll
-    for (int j = 0; j < kNI; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < kNI; ++j) acc[i][j] = f32x4{};
   const int kt_n = K / kBK;
   if (!kIssued) tile_prologue(la, lb, K, lds);
   if (kt_n > 1)
@@ -293,15 +315,13 @@ __device__ __forceinline__ void tile_mainloop(const LA& la, const LB& lb, int K,
   else
     wait_vm0();
   __syncthreads();
-  bf16x8 a0[kMI], b0[kNI], a1[kMI], b1[kNI];
-  ra.read(lds, 0, lane, a0);
+  bf16x8 a[kMI], b0[kNI], b1[kNI];
+  ra.read(lds, 0, lane, a);
   rb.read(lds + kOpBytes, 0, lane, b0);
-  int kt = 0;
-  for (; kt < kt_n - 2; ++kt)
-    mainloop_stage<A_KMAJ, B_KMAJ, true, true>(kt, la, lb, ra, rb, lds, wave, lane, acc, a0, b0, a1, b1);
-  if (kt_n >= 2)
-    mainloop_stage<A_KMAJ, B_KMAJ, false, true>(kt_n - 2, la, lb, ra, rb, lds, wave, lane, acc, a0, b0, a1, b1);
-  mainloop_stage<A_KMAJ, B_KMAJ, false, false>(kt_n - 1, la, lb, ra, rb, lds, wave, lane, acc, a0, b0, a1, b1);
+  // one loop body (no peeled last stages): it keeps the register allocation
+  // within the 256 registers of a wave without spills
+  for (int kt = 0; kt < kt_n; ++kt)
+    mainloop_stage<A_KMAJ, B_KMAJ>(kt, kt_n, la, lb, ra, rb, lds, wave, lane, acc, a, b0, b1);
 }
 
 // Tile (r, c) of workgroup b within a problem of rows x cols tiles occupying
@@ -326,10 +346,10 @@ __device__ __forceinline__ void xcd_tile(int b, int rows, int cols, int& r, int&
 
 // Row / column (within the 256x256 tile) of accumulator element e of block (i, j).
 __device__ __forceinline__ int acc_row(int wave, int lane, int i, int e) {
-  return (wave / kWN) * kWaveM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+  return (wave / kWN) * kWaveM + i * kBlk + 4 * (lane >> 4) + e;
 }
 __device__ __forceinline__ int acc_col(int wave, int lane, int j) {
-  return (wave % kWN) * kWaveN + j * 32 + (lane & 31);
+  return (wave % kWN) * kWaveN + j * kBlk + (lane & 15);
 }
 
 }  // namespace lce
