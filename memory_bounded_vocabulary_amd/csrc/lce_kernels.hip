@@ -382,61 +382,63 @@ __device__ __forceinline__ void recompute_g_tile(const BwdGArgs& a, int id, LCE_
 // C[m0 + r][n0 + c] for r < m_valid - m0, c < n_valid - n0 (n_valid a multiple
 // of 4). The tile goes through LDS in two halves of 128 rows (the rows of the
 // waves with wm = 0, then wm = 1), so that global memory sees 16-byte accesses
-// along whole rows, and all of a thread's loads of C are issued before the
-// first of them is waited for. LDS row r holds the 256 floats of the row, with
-// column c stored at c ^ (16 ((r >> 2) & 3)), so the four 16-lane groups of an
-// accumulator write (rows r, r + 4, r + 8, r + 12, 16 columns each) use
-// different banks. Needs the 128 KB of LDS free (the main loop ends on a
-// barrier).
-// kIt 16-byte chunks of one 128-row half, in batches of kBatch: a batch's
-// loads of C are all issued before the first is waited for.
-template <int kIt, bool kFull, bool kAcc>
-__device__ __forceinline__ void rmw_half(float* __restrict__ C, int ldc, int r0, int m_valid, int n0, int n_valid,
-                                         const float* tile) {
-  constexpr int kBatch = 8;
+// along whole rows. For each half, a thread issues all of its loads of C
+// before the half is staged, so they fly while the accumulators are written
+// to LDS and the half costs one round trip to memory. LDS row r holds the 256
+// floats of the row, with column c stored at c ^ (16 ((r >> 2) & 3)), so the
+// four 16-lane groups of an accumulator write (rows r, r + 4, r + 8, r + 12,
+// 16 columns each) use different banks. Needs the 128 KB of LDS free (the
+// main loop ends on a barrier).
+// Thread t handles 16-byte chunk (t & 63) of rows (t >> 6) + 8 k, k < kIt.
+template <int kIt, bool kFull>
+__device__ __forceinline__ void load_half(const float* __restrict__ C, int ldc, int r0, int m_valid, int n0,
+                                          int n_valid, float4 (&old)[kIt]) {
   const int c = threadIdx.x & 63;
   const int gc = n0 + 4 * c;
 #pragma unroll
-  for (int b0 = 0; b0 < kIt; b0 += kBatch) {
-    float4 old[kBatch];
-    if (kAcc) {
+  for (int k = 0; k < kIt; ++k) {
+    const int gr = r0 + k * (kThreads / 64) + (threadIdx.x >> 6);
+    old[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (kFull || (gr < m_valid && gc < n_valid)) old[k] = *reinterpret_cast<const float4*>(C + (size_t)gr * ldc + gc);
+  }
+}
+template <int kIt, bool kFull, bool kAcc>
+__device__ __forceinline__ void store_half(float* __restrict__ C, int ldc, int r0, int m_valid, int n0, int n_valid,
+                                           const float* tile, const float4 (&old)[kIt]) {
+  const int c = threadIdx.x & 63;
+  const int gc = n0 + 4 * c;
 #pragma unroll
-      for (int k = 0; k < kBatch; ++k) {
-        const int r = (b0 + k) * (kThreads / 64) + (threadIdx.x >> 6);
-        const int gr = r0 + r;
-        old[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        if (kFull || (gr < m_valid && gc < n_valid)) old[k] = *reinterpret_cast<const float4*>(C + (size_t)gr * ldc + gc);
+  for (int k = 0; k < kIt; ++k) {
+    const int r = k * (kThreads / 64) + (threadIdx.x >> 6);
+    const int gr = r0 + r;
+    if (kFull || (gr < m_valid && gc < n_valid)) {
+      float4 v = *reinterpret_cast<const float4*>(tile + r * 256 + 4 * (c ^ (4 * ((r >> 2) & 3))));
+      if (kAcc) {
+        v.x += old[k].x;
+        v.y += old[k].y;
+        v.z += old[k].z;
+        v.w += old[k].w;
       }
-    }
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const int r = (b0 + k) * (kThreads / 64) + (threadIdx.x >> 6);
-      const int gr = r0 + r;
-      if (kFull || (gr < m_valid && gc < n_valid)) {
-        float4 v = *reinterpret_cast<const float4*>(tile + r * 256 + 4 * (c ^ (4 * ((r >> 2) & 3))));
-        if (kAcc) {
-          v.x += old[k].x;
-          v.y += old[k].y;
-          v.z += old[k].z;
-          v.w += old[k].w;
-        }
-        // non-temporal: the next add to this tile comes from a later launch
-        const f32x4 nv = {v.x, v.y, v.z, v.w};
-        __builtin_nontemporal_store(nv, reinterpret_cast<f32x4*>(C + (size_t)gr * ldc + gc));
-      }
+      // non-temporal: the next add to this tile comes from a later launch
+      const f32x4 nv = {v.x, v.y, v.z, v.w};
+      __builtin_nontemporal_store(nv, reinterpret_cast<f32x4*>(C + (size_t)gr * ldc + gc));
     }
   }
 }
 
-__device__ __forceinline__ void store_tile(const Acc& acc, float* __restrict__ C, int ldc, int m0, int m_valid,
-                                           int n0, int n_valid, int accumulate, char* ldsg) {
+template <bool kFull, bool kAcc>
+__device__ __forceinline__ void store_tile_impl(const Acc& acc, float* __restrict__ C, int ldc, int m0, int m_valid,
+                                                int n0, int n_valid, char* ldsg) {
   const int wave = wave_id();
   const int lane = lane_id();
   const int wm = wave / kWN, wn = wave % kWN;
-  const bool full = m0 + kBM <= m_valid && n0 + kBN <= n_valid;
+  constexpr int kIt = 128 * 64 / kThreads;  // 16-byte chunks per thread and half
   float* tile = reinterpret_cast<float*>(ldsg);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
+    const int r0 = m0 + 128 * h;
+    float4 old[kIt];
+    if (kAcc) load_half<kIt, kFull>(C, ldc, r0, m_valid, n0, n_valid, old);
     if (wm == h) {
 #pragma unroll
       for (int i = 0; i < kMI; ++i)
@@ -451,18 +453,22 @@ __device__ __forceinline__ void store_tile(const Acc& acc, float* __restrict__ C
         }
     }
     __syncthreads();
-    constexpr int kIt = 128 * 64 / kThreads;  // 16-byte chunks per thread
-    const int r0 = m0 + 128 * h;
-    if (full && accumulate)
-      rmw_half<kIt, true, true>(C, ldc, r0, m_valid, n0, n_valid, tile);
-    else if (full)
-      rmw_half<kIt, true, false>(C, ldc, r0, m_valid, n0, n_valid, tile);
-    else if (accumulate)
-      rmw_half<kIt, false, true>(C, ldc, r0, m_valid, n0, n_valid, tile);
-    else
-      rmw_half<kIt, false, false>(C, ldc, r0, m_valid, n0, n_valid, tile);
+    store_half<kIt, kFull, kAcc>(C, ldc, r0, m_valid, n0, n_valid, tile, old);
     __syncthreads();
   }
+}
+
+__device__ __forceinline__ void store_tile(const Acc& acc, float* __restrict__ C, int ldc, int m0, int m_valid,
+                                           int n0, int n_valid, int accumulate, char* ldsg) {
+  const bool full = m0 + kBM <= m_valid && n0 + kBN <= n_valid;
+  if (full && accumulate)
+    store_tile_impl<true, true>(acc, C, ldc, m0, m_valid, n0, n_valid, ldsg);
+  else if (full)
+    store_tile_impl<true, false>(acc, C, ldc, m0, m_valid, n0, n_valid, ldsg);
+  else if (accumulate)
+    store_tile_impl<false, true>(acc, C, ldc, m0, m_valid, n0, n_valid, ldsg);
+  else
+    store_tile_impl<false, false>(acc, C, ldc, m0, m_valid, n0, n_valid, ldsg);
 }
 
 __device__ __forceinline__ void grad_tile(const GradArgs& a, int id, LCE_LDS char* lds, char* ldsg) {
