@@ -25,8 +25,15 @@
 //
 // LDS layouts (one operand, one stage, 32 KB):
 //  K-contiguous: 256 rows x 128 bytes (64 bf16 of K), as 16-byte chunks; chunk
-//    kc of row r sits in slot kc ^ swz(r), so the 16-byte fragment reads of 8
-//    (and 16) consecutive rows fall in distinct banks.
+//    kc of row r sits in slot kc ^ swz(r). A fragment read has lane l read
+//    chunk 4 ks + l / 16 of row l % 16 (of a 16-row block). The LDS serves a
+//    16-byte read in four passes of 256 bytes (64 banks); the bank counters
+//    show that lanes l and l + 32 share a pass (eight lanes from each half).
+//    swz permutes row bits 1..3 into slot bits 0..2 so that both the 16
+//    consecutive lanes and the 8 + 8 lanes of a pass fall in distinct banks:
+//    the even (and the odd) rows of a 16-row block get 8 different swizzles,
+//    and rows 0, 2, 4, 6 (or 8, 10, 12, 14) get swizzles that stay distinct
+//    after XOR with 2, the chunk difference between lanes l and l + 32.
 //  K-major: 64 rows (k) x 512 bytes (256 bf16 of m); 16-byte chunk c of row k
 //    sits in slot c ^ kmaj_swz(k), so the four 32-byte row segments one 16-lane
 //    group of a transposing read touches (rows k..k+3) fall in distinct banks.
@@ -54,7 +61,7 @@ constexpr int kNI = kWaveN / kBlk;           // 4 accumulator columns of blocks
 
 typedef f32x4 Acc[kMI][kNI];
 
-__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) & 1) | ((r >> 2) & 2) | (r & 4); }
 __device__ __forceinline__ int kmaj_swz(int k) { return (2 * (k & 3)) ^ (8 * (k & 1)); }
 
 // ---- global -> LDS loaders ------------------------------------------------
@@ -72,22 +79,22 @@ struct KContigLoader {
   uint32_t ld2;   // row pitch in bytes
   int row;        // this lane's row for load 0 (absolute)
   int last;       // last valid row
-  uint32_t kc16;  // byte offset of this lane's chunk for even j (odd j: ^ 16)
+  uint32_t kc16;  // byte offset of this lane's chunk for even j (odd j: ^ 32)
 
   __device__ __forceinline__ void init(const uint16_t* p, int ld, int row0, int rows_valid, int wave, int lane) {
     base = reinterpret_cast<const char*>(p);
     ld2 = (uint32_t)ld * 2u;
     row = row0 + wave * 32 + (lane >> 3);
     last = rows_valid - 1;
-    // chunk (lane & 7) of row r sits in slot (lane & 7) ^ swz(r); for these rows
-    // swz(r) = (lane >> 3) ^ (j & 1)
-    kc16 = (uint32_t)(((lane & 7) ^ (lane >> 3)) * 16);
+    // chunk (lane & 7) of row r sits in slot (lane & 7) ^ swz(r); these rows
+    // have r % 16 = 8 (j & 1) + lane / 8, so swz(r) = swz(lane / 8) ^ 2 (j & 1)
+    kc16 = (uint32_t)(((lane & 7) ^ swz(lane >> 3)) * 16);
   }
   __device__ __forceinline__ void issue(int k0, LCE_LDS char* tile, int wave) const {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t gr = (uint32_t)min(row + 8 * j, last);
-      g2lds16(base, gr * ld2 + (kc16 ^ (16u * (j & 1))) + (uint32_t)k0 * 2u, tile + (wave * 4 + j) * 1024);
+      g2lds16(base, gr * ld2 + (kc16 ^ (32u * (j & 1))) + (uint32_t)k0 * 2u, tile + (wave * 4 + j) * 1024);
     }
   }
 };
