@@ -65,14 +65,21 @@ __device__ __forceinline__ int swz(int r) { return ((r >> 1) & 1) | ((r >> 2) & 
 __device__ __forceinline__ int kmaj_swz(int k) { return (2 * (k & 3)) ^ (8 * (k & 1)); }
 
 // ---- global -> LDS loaders ------------------------------------------------
-// Each wave issues 4 loads of 1 KB (64 lanes x 16 bytes) per operand and stage.
+// Only the first kLoadWaves waves (one per SIMD) issue a stage's loads, kLoadJ
+// loads of 1 KB (64 lanes x 16 bytes) per operand each. After a stage barrier
+// the other wave on each SIMD starts its MFMAs at once while the loading wave
+// issues, so the MFMA pipe does not sit idle behind the issue of the loads;
+// the skew this leaves between the two waves of a SIMD is absorbed at the next
+// barrier, where the late wave's MFMAs keep the pipe busy.
+constexpr int kLoadWaves = 4;
+constexpr int kLoadJ = (kOpBytes / 1024) / kLoadWaves;  // 8
 
 // K-contiguous operand: tile rows row0..row0+255 of a [rows][ld] bf16 matrix.
 // Rows at or past rows_valid are clamped to the last valid row: they load real
 // (finite) data whose results the epilogues discard or whose partner operand
-// is zero there. Load j of a wave fills tile rows 32 wave + 8 j + lane / 8; the
-// per-lane state is two registers, and each load's address is formed when it
-// is issued (a few VALU per 16-byte load), which keeps the main loop's
+// is zero there. Load j of loading wave w fills tile rows 64 w + 8 j + lane / 8;
+// the per-lane state is two registers, and each load's address is formed when
+// it is issued (a few VALU per 16-byte load), which keeps the main loop's
 // register footprint small.
 struct KContigLoader {
   const char* base;
@@ -84,26 +91,35 @@ struct KContigLoader {
   __device__ __forceinline__ void init(const uint16_t* p, int ld, int row0, int rows_valid, int wave, int lane) {
     base = reinterpret_cast<const char*>(p);
     ld2 = (uint32_t)ld * 2u;
-    row = row0 + wave * 32 + (lane >> 3);
+    row = row0 + wave * (8 * kLoadJ) + (lane >> 3);
     last = rows_valid - 1;
     // chunk (lane & 7) of row r sits in slot (lane & 7) ^ swz(r); these rows
     // have r % 16 = 8 (j & 1) + lane / 8, so swz(r) = swz(lane / 8) ^ 2 (j & 1)
     kc16 = (uint32_t)(((lane & 7) ^ swz(lane >> 3)) * 16);
   }
+  // kOpaque: the row goes through an empty asm first, so that the kLoadJ
+  // addresses are formed at each issue instead of being hoisted out of the
+  // main loop as invariants. Hoisting saves VALU but holds 8 registers per
+  // loader across the loop, which the forward (running state per token in
+  // registers) cannot spare.
+  template <bool kOpaque = false>
   __device__ __forceinline__ void issue(int k0, LCE_LDS char* tile, int wave) const {
+    if (wave >= kLoadWaves) return;
+    int r = row;
+    if (kOpaque) asm volatile("" : "+v"(r));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t gr = (uint32_t)min(row + 8 * j, last);
-      g2lds16(base, gr * ld2 + (kc16 ^ (32u * (j & 1))) + (uint32_t)k0 * 2u, tile + (wave * 4 + j) * 1024);
+    for (int j = 0; j < kLoadJ; ++j) {
+      const uint32_t gr = (uint32_t)min(r + 8 * j, last);
+      g2lds16(base, gr * ld2 + (kc16 ^ (32u * (j & 1))) + (uint32_t)k0 * 2u, tile + (wave * kLoadJ + j) * 1024);
     }
   }
 };
 
 // K-major operand: element (m, k) at p[k * ld + m]; the tile covers columns
 // m0..m0+255 and rows k0..k0+63. Columns past m_valid (a multiple of 8) and
-// rows past k_valid are clamped to the last valid ones. Load j of a wave fills
-// tile rows 8 wave + 2 j and 8 wave + 2 j + 1 (lanes 0-31 and 32-63), 16 bytes
-// per lane.
+// rows past k_valid are clamped to the last valid ones. Load j of loading wave
+// w fills tile rows 2 q and 2 q + 1 (lanes 0-31 and 32-63), q = kLoadJ w + j,
+// 16 bytes per lane.
 struct KMajorLoader {
   const char* base;
   uint32_t ld2;       // row pitch in bytes
@@ -116,7 +132,7 @@ struct KMajorLoader {
     base = reinterpret_cast<const char*>(p);
     ld2 = (uint32_t)ld * 2u;
     k_last = k_valid - 1;
-    row = 8 * wave + (lane >> 5);
+    row = 2 * kLoadJ * wave + (lane >> 5);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int r = row + 2 * h;             // kmaj_swz depends on r & 3 only
@@ -124,11 +140,15 @@ struct KMajorLoader {
       col[h] = (uint32_t)min(m0 + c * 8, m_valid - 8) * 2u;
     }
   }
+  template <bool kOpaque = false>
   __device__ __forceinline__ void issue(int k0, LCE_LDS char* tile, int wave) const {
+    if (wave >= kLoadWaves) return;
+    int r = row;  // kOpaque: as in KContigLoader::issue
+    if (kOpaque) asm volatile("" : "+v"(r));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t kr = (uint32_t)min(k0 + row + 2 * j, k_last);
-      g2lds16(base, kr * ld2 + col[j & 1], tile + (wave * 4 + j) * 1024);
+    for (int j = 0; j < kLoadJ; ++j) {
+      const uint32_t kr = (uint32_t)min(k0 + r + 2 * j, k_last);
+      g2lds16(base, kr * ld2 + col[j & 1], tile + (wave * kLoadJ + j) * 1024);
     }
   }
 };
@@ -247,7 +267,7 @@ __device__ __forceinline__ void interleave_from() {
 // buffer too, whatever it holds then (the values are never used): keeping
 // those reads unconditional keeps them in the same basic block as the MFMAs
 // they interleave with.
-template <bool A_KMAJ, bool B_KMAJ, class LA, class LB, class RA, class RB>
+template <bool A_KMAJ, bool B_KMAJ, bool kOpaque, class LA, class LB, class RA, class RB>
 __device__ __forceinline__ void mainloop_stage(int kt, int kt_n, const LA& la, const LB& lb, const RA& ra,
                                                const RB& rb, LCE_LDS char* lds, int wave, int lane, Acc& acc,
                                                bf16x8 (&a)[kMI], bf16x8 (&b0)[kNI], bf16x8 (&b1)[kNI]) {
@@ -271,8 +291,8 @@ __device__ __forceinline__ void mainloop_stage(int kt, int kt_n, const LA& la, c
   __syncthreads();
   __builtin_amdgcn_sched_barrier(0);
   if (kt + 2 < kt_n) {
-    la.issue((kt + 2) * kBK, cur, wave);
-    lb.issue((kt + 2) * kBK, cur + kOpBytes, wave);
+    la.template issue<kOpaque>((kt + 2) * kBK, cur, wave);
+    lb.template issue<kOpaque>((kt + 2) * kBK, cur + kOpBytes, wave);
   }
   mma_step<kMI, kNI>(acc, a, b1);
   rb.read(nxt + kOpBytes, 0, lane, b0);
@@ -302,7 +322,7 @@ __device__ __forceinline__ void tile_prologue(const LA& la, const LB& lb, int K,
 // load into LDS is in flight, so both LDS stages are free for the caller (the
 // discarded reads of the last stage may still be in flight: they read, never
 // write, and nothing uses what they return).
-template <bool A_KMAJ, bool B_KMAJ, bool kIssued = false, class LA, class LB>
+template <bool A_KMAJ, bool B_KMAJ, bool kIssued = false, bool kOpaque = false, class LA, class LB>
 __device__ __forceinline__ void tile_mainloop(const LA& la, const LB& lb, int K, LCE_LDS char* lds, Acc& acc) {
   const int wave = wave_id();
   const int lane = lane_id();
@@ -318,7 +338,7 @@ __device__ __forceinline__ void tile_mainloop(const LA& la, const LB& lb, int K,
   const int kt_n = K / kBK;
   if (!kIssued) tile_prologue(la, lb, K, lds);
   if (kt_n > 1)
-    wait_vm<8>();  // stage 0 landed (the 8 loads of stage 1 may still fly)
+    wait_vm<2 * kLoadJ>();  // stage 0 landed (the loads of stage 1 may still fly)
   else
     wait_vm0();
   __syncthreads();
@@ -328,7 +348,7 @@ __device__ __forceinline__ void tile_mainloop(const LA& la, const LB& lb, int K,
   // one loop body (no peeled last stages): it keeps the register allocation
   // within the 256 registers of a wave without spills
   for (int kt = 0; kt < kt_n; ++kt)
-    mainloop_stage<A_KMAJ, B_KMAJ>(kt, kt_n, la, lb, ra, rb, lds, wave, lane, acc, a, b0, b1);
+    mainloop_stage<A_KMAJ, B_KMAJ, kOpaque>(kt, kt_n, la, lb, ra, rb, lds, wave, lane, acc, a, b0, b1);
 }
 
 // Tile (r, c) of workgroup b within a problem of rows x cols tiles occupying
