@@ -35,8 +35,12 @@
 //    and rows 0, 2, 4, 6 (or 8, 10, 12, 14) get swizzles that stay distinct
 //    after XOR with 2, the chunk difference between lanes l and l + 32.
 //  K-major: 64 rows (k) x 512 bytes (256 bf16 of m); 16-byte chunk c of row k
-//    sits in slot c ^ kmaj_swz(k), so the four 32-byte row segments one 16-lane
-//    group of a transposing read touches (rows k..k+3) fall in distinct banks.
+//    sits in slot c ^ kmaj_swz(k). A transposing read has 16-lane group g read
+//    rows 8 g + 0..3 (then + 4..7), 32 bytes each. kmaj_swz spreads the four
+//    rows of a group over distinct banks, and its bit-3/bit-4 term moves groups
+//    g and g ^ 1, and g and g ^ 2, onto the complementary banks, so that a
+//    pass of 32 lanes (either lanes 0-31, or l and l + 32) is conflict-free
+//    too.
 #pragma once
 #include "cdna4.hpp"
 
@@ -62,7 +66,7 @@ constexpr int kNI = kWaveN / kBlk;           // 4 accumulator columns of blocks
 typedef f32x4 Acc[kMI][kNI];
 
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) & 1) | ((r >> 2) & 2) | (r & 4); }
-__device__ __forceinline__ int kmaj_swz(int k) { return (2 * (k & 3)) ^ (8 * (k & 1)); }
+__device__ __forceinline__ int kmaj_swz(int k) { return (2 * (k & 3)) ^ (8 * (k & 1)) ^ (2 * (((k >> 3) ^ (k >> 4)) & 1)); }
 
 // ---- global -> LDS loaders ------------------------------------------------
 // Only the first kLoadWaves waves (one per SIMD) issue a stage's loads, kLoadJ
@@ -118,8 +122,10 @@ struct KContigLoader {
 // K-major operand: element (m, k) at p[k * ld + m]; the tile covers columns
 // m0..m0+255 and rows k0..k0+63. Columns past m_valid (a multiple of 8) and
 // rows past k_valid are clamped to the last valid ones. Load j of loading wave
-// w fills tile rows 2 q and 2 q + 1 (lanes 0-31 and 32-63), q = kLoadJ w + j,
-// 16 bytes per lane.
+// w fills tile rows 2 q and 2 q + 1 (lanes 0-31 and 32-63), 16 bytes per lane,
+// q = 4 w + (j & 3) + 16 (j >> 2): the wave's rows are 8 w .. 8 w + 7 and
+// 32 + 8 w .. 32 + 8 w + 7, which share bits 3 and 4 of the row, so kmaj_swz
+// of a lane's row takes only two values (by j & 1).
 struct KMajorLoader {
   const char* base;
   uint32_t ld2;       // row pitch in bytes
@@ -132,10 +138,11 @@ struct KMajorLoader {
     base = reinterpret_cast<const char*>(p);
     ld2 = (uint32_t)ld * 2u;
     k_last = k_valid - 1;
-    row = 2 * kLoadJ * wave + (lane >> 5);
+    static_assert(kLoadWaves == 4 && kLoadJ == 8, "row assignment written for 4 loading waves x 8 loads");
+    row = 8 * wave + (lane >> 5);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int r = row + 2 * h;             // kmaj_swz depends on r & 3 only
+      const int r = row + 2 * h;             // same row bits 0, 1, 3, 4 as the rows of loads with j & 1 = h
       const int c = (lane & 31) ^ kmaj_swz(r);
       col[h] = (uint32_t)min(m0 + c * 8, m_valid - 8) * 2u;
     }
@@ -147,8 +154,8 @@ struct KMajorLoader {
     if (kOpaque) asm volatile("" : "+v"(r));
 #pragma unroll
     for (int j = 0; j < kLoadJ; ++j) {
-      const uint32_t kr = (uint32_t)min(k0 + r + 2 * j, k_last);
-      g2lds16(base, kr * ld2 + col[j & 1], tile + (wave * kLoadJ + j) * 1024);
+      const uint32_t kr = (uint32_t)min(k0 + r + 2 * (j & 3) + 32 * (j >> 2), k_last);
+      g2lds16(base, kr * ld2 + col[j & 1], tile + (4 * wave + (j & 3) + 16 * (j >> 2)) * 1024);
     }
   }
 };
