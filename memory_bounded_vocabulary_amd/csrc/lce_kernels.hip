@@ -296,6 +296,35 @@ __global__ __launch_bounds__(256) void bwd_scale_kernel(const int* __restrict__ 
 // G in different buffers: the short recompute tiles fill in behind the long
 // gradient tiles, and the backward needs one launch per unit instead of two.
 // --------------------------------------------------------------------------
+// G of one recomputed tile into the LDS staging area: token row tok holds the
+// tile's 256 vocabulary values as bf16, 16-byte chunk c in slot c ^ (tok & 31).
+template <bool kMask, bool kOneHot>
+__device__ __forceinline__ void stage_g(const Acc& acc, const float (&lse2)[kNI], const float (&g)[kNI],
+                                        const int (&tcol)[kNI], int live, char* ldsg) {
+  const int wave = wave_id();
+  const int lane = lane_id();
+  const int wm = wave / kWN, wn = wave % kWN;
+#pragma unroll
+  for (int j = 0; j < kNI; ++j) {
+    const int tok = wn * kWaveN + kBlk * j + (lane & 15);  // token row of the staged tile
+#pragma unroll
+    for (int i = 0; i < kMI; ++i) {
+      const int r0 = wm * kWaveM + kBlk * i + 4 * (lane >> 4);  // 4 consecutive vocabulary rows
+      float gv[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = r0 + q;
+        const float p = fast_exp2(fmaf(acc[i][j][q], kLog2e, -lse2[j]));
+        const float v = kOneHot ? g[j] * (p - (r == tcol[j] ? 1.0f : 0.0f)) : g[j] * p;
+        gv[q] = (!kMask || r < live) ? v : 0.0f;
+      }
+      const int slot = (r0 >> 3) ^ (tok & 31);
+      uint2 packed = make_uint2(pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3]));
+      *reinterpret_cast<uint2*>(ldsg + tok * 512 + slot * 16 + (r0 & 7) * 2) = packed;
+    }
+  }
+}
+
 __device__ __forceinline__ void recompute_g_tile(const BwdGArgs& a, int id, LCE_LDS char* lds, char* ldsg) {
   const int wave = wave_id();
   const int lane = lane_id();
@@ -347,24 +376,24 @@ __device__ __forceinline__ void recompute_g_tile(const BwdGArgs& a, int id, LCE_
     }
   }
   const int live = a.vc - tv * kBM;  // vocabulary rows of this tile inside the chunk
+  // The row mask matters only in a chunk's last, partial tile, and the one-hot
+  // only in a wave whose 128 vocabulary rows hold some lane's target: both are
+  // uniform over the wave, so the common case skips their compares (the
+  // values are the same: p - 0 is p).
+  bool has_target = false;
 #pragma unroll
-  for (int j = 0; j < kNI; ++j) {
-    const int tok = wn * kWaveN + kBlk * j + (lane & 15);  // token row of the staged tile
-#pragma unroll
-    for (int i = 0; i < kMI; ++i) {
-      const int r0 = wm * kWaveM + kBlk * i + 4 * (lane >> 4);  // 4 consecutive vocabulary rows
-      float gv[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = r0 + q;
-        const float p = fast_exp2(fmaf(acc[i][j][q], kLog2e, -lse2[j]));
-        const float v = g[j] * (p - (r == tcol[j] ? 1.0f : 0.0f));
-        gv[q] = r < live ? v : 0.0f;
-      }
-      const int slot = (r0 >> 3) ^ (tok & 31);
-      uint2 packed = make_uint2(pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3]));
-      *reinterpret_cast<uint2*>(ldsg + tok * 512 + slot * 16 + (r0 & 7) * 2) = packed;
-    }
+  for (int j = 0; j < kNI; ++j) has_target |= tcol[j] >= wm * kWaveM && tcol[j] < wm * kWaveM + kWaveM;
+  const bool one_hot = __any(has_target);
+  if (live < kBM) {
+    if (one_hot)
+      stage_g<true, true>(acc, lse2, g, tcol, live, ldsg);
+    else
+      stage_g<true, false>(acc, lse2, g, tcol, live, ldsg);
+  } else {
+    if (one_hot)
+      stage_g<false, true>(acc, lse2, g, tcol, live, ldsg);
+    else
+      stage_g<false, false>(acc, lse2, g, tcol, live, ldsg);
   }
   __syncthreads();
   uint16_t* gt = a.G + (size_t)tt * kBN * a.ldg + (size_t)tv * kBM;
