@@ -214,7 +214,8 @@ struct KMajorReader {
     (void)lane;
 #pragma unroll
     for (int i = I0; i < I1; ++i) {
-      // rows k, k + 4 and k + 32 ks have the same (k & 3), so the same swizzle
+      // rows k, k + 4 and k + 32 ks share bits 0, 1, 3 and 4 (k % 8 < 4), so
+      // the same swizzle
       const bf16x4 lo = ds_read_tr16(tile + off[i] + ks * kKStep * 512);
       const bf16x4 hi = ds_read_tr16(tile + off[i] + ks * kKStep * 512 + 4 * 512);
       f[i - I0] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
