@@ -16,6 +16,11 @@ What each check pins, and where the fact comes from:
 * zero_weight: W = 0 makes every logit 0, so each valid token's loss is ln V,
   dX = 0, and dW_v = g (sum of valid x_i / V - sum of valid x_i with t_i = v).
 * logistic: V = 2 reduces to the logistic loss log(1 + exp(y_other - y_t)).
+* bf16_widening: the widening of bfloat16 bit patterns, over all 65536 of
+  them, against the format's own definition (1 sign bit, 8 exponent bits with
+  bias 127, 7 fraction bits; subnormals at exponent field 0; all-ones exponent
+  for infinities and NaN) evaluated with math.ldexp, and against torch's
+  bfloat16 -> float64 conversion; plus hand-checked patterns.
 * invariants: softmax-minus-one-hot rows sum to 0 (so sum_v dW_v = 0);
   adding one vector c to every vocabulary row leaves loss and gradients
   unchanged; an ignored row contributes nothing (equal to dropping it while
@@ -78,6 +83,42 @@ def check_brute_force(orc, seeds=range(6)):
             np.testing.assert_allclose(r.lse, lse, rtol=1e-12, atol=1e-12)
             np.testing.assert_allclose(r.d_hidden, dx, rtol=1e-10, atol=1e-13)
             np.testing.assert_allclose(r.d_weight, dw, rtol=1e-10, atol=1e-13)
+
+
+def _bf16_by_definition(bits):
+    """Value of one bfloat16 bit pattern from the format's fields."""
+    sign = -1.0 if bits >> 15 else 1.0
+    e = (bits >> 7) & 0xFF
+    f = bits & 0x7F
+    if e == 0xFF:
+        return sign * math.inf if f == 0 else math.nan
+    if e == 0:
+        return sign * math.ldexp(f, -126 - 7)          # subnormal: 0.f x 2^-126
+    return sign * math.ldexp(128 + f, e - 127 - 7)     # normal: 1.f x 2^(e - 127)
+
+
+def check_bf16_widening(orc):
+    import torch
+    allbits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(invalid="ignore"):      # signalling-NaN patterns are widened to NaN
+        got = orc.bf16_to_f64(allbits)
+    assert got.dtype == np.float64 and got.shape == (1 << 16,)
+    ref = np.array([_bf16_by_definition(int(b)) for b in range(1 << 16)])
+    lib = torch.from_numpy(allbits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    for expect in (ref, lib):
+        nan = np.isnan(expect)
+        assert np.array_equal(np.isnan(got), nan)
+        assert np.array_equal(got[~nan], expect[~nan])
+        # signed zeros keep their sign
+        assert np.array_equal(np.signbit(got[~nan]), np.signbit(expect[~nan]))
+    hand = {0x3F80: 1.0, 0xC020: -2.5, 0x0001: 2.0 ** -133, 0x7F80: math.inf, 0xFF80: -math.inf,
+            0x4049: 3.140625, 0x0080: 2.0 ** -126, 0x7F7F: (2.0 - 2.0 ** -7) * 2.0 ** 127}
+    for b, v in hand.items():
+        assert orc.bf16_to_f64(np.array([b], dtype=np.uint16))[0] == v, hex(b)
+    assert math.copysign(1.0, orc.bf16_to_f64(np.array([0x8000], dtype=np.uint16))[0]) == -1.0
+    assert math.isnan(orc.bf16_to_f64(np.array([0x7FC0], dtype=np.uint16))[0])
+    # a 2-D array keeps its shape
+    assert orc.bf16_to_f64(np.array([[0x3F80, 0x4000]], dtype=np.uint16)).tolist() == [[1.0, 2.0]]
 
 
 def check_torch_reference(orc, x, w, t, tol=1e-10, row_block=None):
@@ -243,7 +284,8 @@ def check_row_samples(orc, seed=6):
 
 
 def all_small_checks(orc):
-    """Every pin that runs in well under a second (used by the planted-mistake test)."""
+    """Every pin that runs in about a second (used by the planted-mistake test)."""
+    check_bf16_widening(orc)
     check_brute_force(orc)
     rng = np.random.default_rng(11)
     x, w, t = rand_instance(rng, 16, 8, 40, ignore=4)

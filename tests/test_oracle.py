@@ -13,6 +13,10 @@ import oracle_pins as pins
 import workloads
 
 
+def test_bf16_widening():
+    pins.check_bf16_widening(oracle)
+
+
 def test_brute_force():
     pins.check_brute_force(oracle)
 
@@ -93,6 +97,9 @@ def test_out_of_range_target_raises():
 # Each entry breaks one step of a copy of the oracle's source. The copy is run
 # through the same pins; every one of them must fail at least one pin.
 MUTANTS = {
+    "bf16 widening shifted by 15": ("<< np.uint32(16)", "<< np.uint32(15)"),
+    "bf16 widening drops the low fraction bit": ("u = np.asarray(bits, dtype=np.uint16).astype(np.uint32)",
+                                                 "u = (np.asarray(bits, dtype=np.uint16) & 0xFFFE).astype(np.uint32)"),
     "lse without the max": ("lse_b = m + np.log(", "lse_b = np.log("),
     "one-hot added, not subtracted": ("p[rows, t[r0 + rows]] -= 1.0", "p[rows, t[r0 + rows]] += 1.0"),
     "target index without block offset": ("z[rows, t[r0 + rows]]", "z[rows, t[rows]]"),
