@@ -190,6 +190,7 @@ def forward(hidden, shards: Sequence, targets, ignore_index: int = -100, order: 
     d = make_dims(n, h, v, p, ignore_index, reduction)
     if workspace is None:
         workspace = alloc_workspace(n, h, v, p, hidden.device, ignore_index, reduction)
+    _require_cuda(workspace)
     token_loss = token_loss or reduction == "none"
     loss = torch.empty((), dtype=torch.float32, device=hidden.device)
     lse = torch.empty(n, dtype=torch.float32, device=hidden.device)
@@ -232,6 +233,8 @@ def backward(hidden, shards: Sequence, targets, lse, dloss, ignore_index: int = 
         dloss = torch.tensor(float(dloss), dtype=torch.float32, device=hidden.device)
     if reduction == "none" and dloss.numel() != n:
         raise ValueError("reduction 'none' takes a per-token dloss of N elements")
+    if reduction != "none" and dloss.numel() != 1:
+        raise ValueError("reductions 'mean' and 'sum' take one dloss value")
     if dloss.dtype != torch.float32 or not dloss.is_contiguous():
         raise ValueError("dloss must be a contiguous fp32 tensor")
     _require_cuda(dloss)
@@ -244,6 +247,7 @@ def backward(hidden, shards: Sequence, targets, lse, dloss, ignore_index: int = 
             raise ValueError(f"gradient buffers must be contiguous {grad_dtype}")
     if tuple(d_hidden.shape) != (n, h) or len(d_shards) != p or any(tuple(g.shape) != (vs, h) for g in d_shards):
         raise ValueError("gradient buffers must match hidden [N, H] and the shards [V/P, H]")
+    _require_cuda(workspace, d_hidden, *d_shards)
     st = lib().lce_backward(ctypes.byref(d), hidden.data_ptr(), _ptr_array([s.data_ptr() for s in shards]),
                             _order_array(order), targets.data_ptr(), lse.data_ptr(), dloss.data_ptr(),
                             d_hidden.data_ptr(), _ptr_array([g.data_ptr() for g in d_shards]),
@@ -252,9 +256,34 @@ def backward(hidden, shards: Sequence, targets, lse, dloss, ignore_index: int = 
     return d_hidden, d_shards
 
 
+def _check_round_tensors(dims: Dims, hidden, shard, targets, lse=None) -> None:
+    """The per-round calls take their sizes from `dims`: the tensors must agree with it."""
+    _check_inputs(hidden, [shard], targets, lse)
+    n, h = hidden.shape
+    if dims.n_shards < 1 or dims.vocab % dims.n_shards:
+        raise ValueError("dims.vocab must be a multiple of dims.n_shards")
+    if int(dims.n_tokens) != n or int(dims.hidden) != h:
+        raise ValueError(f"dims (n_tokens={dims.n_tokens}, hidden={dims.hidden}) do not match hidden {tuple(hidden.shape)}")
+    if int(dims.vocab) // int(dims.n_shards) != shard.shape[0]:
+        raise ValueError(f"dims give {dims.vocab // dims.n_shards} rows per shard; the shard has {shard.shape[0]}")
+
+
+def _check_workspace(dims: Dims, workspace) -> None:
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    if _nbytes(workspace) < int(lib().lce_workspace_bytes(ctypes.byref(dims))):
+        raise ValueError("workspace is smaller than workspace_bytes(dims)")
+
+
+def _grad_dtype(dims: Dims):
+    import torch
+    return torch.bfloat16 if int(dims.flags) & FLAG_BF16_GRADS else torch.float32
+
+
 def fwd_round(dims: Dims, round_: int, shard_index: int, hidden, shard, targets, workspace, stream=None) -> None:
     """One forward ring round: fold `shard` (id `shard_index`) into the state held in `workspace`."""
-    _check_inputs(hidden, [shard], targets)
+    _check_round_tensors(dims, hidden, shard, targets)
+    _check_workspace(dims, workspace)
     _require_cuda(hidden, shard, targets, workspace)
     _check(lib().lce_fwd_round(ctypes.byref(dims), int(round_), int(shard_index), hidden.data_ptr(),
                                shard.data_ptr(), targets.data_ptr(), workspace.data_ptr(), _nbytes(workspace),
@@ -264,8 +293,11 @@ def fwd_round(dims: Dims, round_: int, shard_index: int, hidden, shard, targets,
 def fwd_finish(dims: Dims, targets, workspace, token_loss: bool = False, stream=None):
     """After the rounds: (loss, lse) or (loss, lse, token_loss) from the state in `workspace`."""
     import torch
-    _require_cuda(targets, workspace)
     n = int(dims.n_tokens)
+    if targets.dim() != 1 or targets.dtype != torch.int32 or not targets.is_contiguous() or targets.shape[0] != n:
+        raise ValueError("targets must be a contiguous int32 [dims.n_tokens] tensor")
+    _check_workspace(dims, workspace)
+    _require_cuda(targets, workspace)
     loss = torch.empty((), dtype=torch.float32, device=targets.device)
     lse = torch.empty(n, dtype=torch.float32, device=targets.device)
     tl = torch.empty(n, dtype=torch.float32, device=targets.device) if token_loss else None
@@ -277,11 +309,23 @@ def fwd_finish(dims: Dims, targets, workspace, token_loss: bool = False, stream=
 
 def bwd_round(dims: Dims, round_: int, shard_index: int, hidden, shard, targets, lse, dloss, d_hidden, d_shard,
               accumulate_dw: bool, workspace, stream=None) -> None:
-    """One backward ring round: d_hidden (+)= G W_shard, d_shard (+)= G^T X for this shard."""
-    _check_inputs(hidden, [shard], targets, lse)
-    for t in (d_hidden, d_shard, dloss, workspace):
-        if not t.is_contiguous():
-            raise ValueError("d_hidden, d_shard, dloss and workspace must be contiguous")
+    """One backward ring round: d_hidden (+)= G W_shard, d_shard (+)= G^T X for this shard.
+
+    Gradient buffers are fp32, or bf16 when dims.flags has FLAG_BF16_GRADS;
+    dloss is one fp32 value (mean / sum) or fp32 [N] (reduction "none")."""
+    import torch
+    _check_round_tensors(dims, hidden, shard, targets, lse)
+    if lse is None:
+        raise ValueError("lse (from the forward) is required")
+    gdt = _grad_dtype(dims)
+    n, h = hidden.shape
+    for name, t, shape in (("d_hidden", d_hidden, (n, h)), ("d_shard", d_shard, tuple(shard.shape))):
+        if t.dtype != gdt or tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {gdt} tensor of shape {shape}")
+    want = n if int(dims.reduction) == REDUCTIONS["none"] else 1
+    if dloss.dtype != torch.float32 or dloss.numel() != want or not dloss.is_contiguous():
+        raise ValueError(f"dloss must be a contiguous fp32 tensor of {want} element(s)")
+    _check_workspace(dims, workspace)
     _require_cuda(hidden, shard, targets, lse, dloss, d_hidden, d_shard, workspace)
     _check(lib().lce_bwd_round(ctypes.byref(dims), int(round_), int(shard_index), hidden.data_ptr(),
                                shard.data_ptr(), targets.data_ptr(), lse.data_ptr(), dloss.data_ptr(),

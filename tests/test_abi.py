@@ -301,3 +301,76 @@ def test_binding_rejects_layouts_the_abi_cannot_take():
         lce.backward(h, sh, t, torch.zeros((7,)), 1.0)
     with pytest.raises(ValueError, match="GPU"):
         lce.forward(h, sh, t)
+
+
+def test_binding_round_calls_check_dims_against_tensors():
+    """The per-round calls take N, H and V/P from dims: a mismatch, a gradient
+    buffer of the wrong dtype or shape, or a dloss of the wrong size is refused
+    before any pointer reaches the library (it would otherwise read or write
+    past a buffer)."""
+    import torch
+    n, h, vs, p = 8, 64, 16, 2
+    x = torch.zeros((n, h), dtype=torch.bfloat16)
+    w = torch.zeros((vs, h), dtype=torch.bfloat16)
+    t = torch.zeros((n,), dtype=torch.int32)
+    lse = torch.zeros((n,))
+    dl = torch.ones(())
+    dims = lce.make_dims(n, h, vs * p, p)
+    ws = torch.zeros(lce.workspace_bytes(n, h, vs * p, p), dtype=torch.uint8)
+    dx, dw = torch.zeros((n, h)), torch.zeros((vs, h))
+
+    def fr(d=dims, **kw):
+        a = dict(hidden=x, shard=w, targets=t, workspace=ws)
+        a.update(kw)
+        lce.fwd_round(d, 0, 0, a["hidden"], a["shard"], a["targets"], a["workspace"])
+
+    def br(d=dims, **kw):
+        a = dict(hidden=x, shard=w, targets=t, lse=lse, dloss=dl, d_hidden=dx, d_shard=dw, workspace=ws)
+        a.update(kw)
+        lce.bwd_round(d, 0, 0, a["hidden"], a["shard"], a["targets"], a["lse"], a["dloss"], a["d_hidden"],
+                      a["d_shard"], False, a["workspace"])
+
+    for bad in (lce.make_dims(n + 8, h, vs * p, p), lce.make_dims(n, 2 * h, vs * p, p),
+                lce.make_dims(n, h, 2 * vs * p, p), lce.make_dims(n, h, vs * p + 1, p)):
+        with pytest.raises(ValueError, match="dims"):
+            fr(bad)
+        with pytest.raises(ValueError, match="dims"):
+            br(bad)
+    with pytest.raises(ValueError, match="targets"):
+        lce.fwd_finish(lce.make_dims(n + 1, h, vs * p, p), t, ws)
+    with pytest.raises(ValueError, match="workspace"):
+        fr(workspace=ws[:-16])
+    with pytest.raises(ValueError, match="workspace"):
+        lce.fwd_finish(dims, t, ws[:16])
+    # bf16 gradient buffers without the bf16 flag (and fp32 ones with it)
+    with pytest.raises(ValueError, match="d_shard"):
+        br(d_shard=dw.bfloat16())
+    with pytest.raises(ValueError, match="d_hidden"):
+        br(d_hidden=dx.bfloat16())
+    d16 = lce.make_dims(n, h, vs * p, p, flags=lce.FLAG_BF16_GRADS)
+    ws16 = torch.zeros(lce.workspace_bytes(n, h, vs * p, p, flags=lce.FLAG_BF16_GRADS), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="d_hidden"):
+        br(d16, workspace=ws16)
+    with pytest.raises(ValueError, match="d_hidden"):
+        br(d_hidden=torch.zeros((n, h + 64)))
+    with pytest.raises(ValueError, match="d_shard"):
+        br(d_shard=torch.zeros((vs + 1, h)))
+    with pytest.raises(ValueError, match="dloss"):
+        br(dloss=torch.ones((n,)))
+    with pytest.raises(ValueError, match="dloss"):
+        br(dloss=torch.ones((), dtype=torch.float64))
+    with pytest.raises(ValueError, match="dloss"):
+        br(lce.make_dims(n, h, vs * p, p, reduction="none"), dloss=dl)
+    with pytest.raises(ValueError, match="lse"):
+        br(lse=torch.zeros((n + 1,)))
+    # consistent host tensors pass every layout check and stop at the device check
+    with pytest.raises(ValueError, match="GPU"):
+        fr()
+    with pytest.raises(ValueError, match="GPU"):
+        br()
+    with pytest.raises(ValueError, match="GPU"):
+        br(d16, workspace=ws16, d_hidden=dx.bfloat16(), d_shard=dw.bfloat16())
+    with pytest.raises(ValueError, match="GPU"):
+        lce.fwd_finish(dims, t, ws)
+    with pytest.raises(ValueError, match="GPU"):
+        lce.backward(x, [w, w], t, lse, torch.ones((n,)))

@@ -153,3 +153,28 @@ def test_empty_batch(reduction):
     assert all(bool((d == 0).all().item()) for d in dws)
     assert all(bool((d == 0).all().item()) for d in dws_r)
     assert all(torch.equal(a, g) for a, g in zip(acc, garbage))
+
+
+def test_binding_refuses_host_buffers_beside_device_inputs():
+    """A host workspace or gradient buffer never reaches the kernels as a pointer."""
+    import torch
+    import memory_bounded_vocabulary_amd as lce
+    b = workloads.make("tiny")
+    hidden, shards, targets = to_device(b)
+    w = b.workload
+    say("host buffers beside device inputs")
+    ws_host = torch.zeros(lce.workspace_bytes(w.n_tokens, w.hidden, w.vocab, w.n_shards), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="GPU"):
+        lce.forward(hidden, shards, targets, workspace=ws_host)
+    loss, lse = lce.forward(hidden, shards, targets)
+    with pytest.raises(ValueError, match="GPU"):
+        lce.backward(hidden, shards, targets, lse, 1.0, workspace=ws_host)
+    with pytest.raises(ValueError, match="GPU"):
+        lce.backward(hidden, shards, targets, lse, 1.0, d_hidden=torch.zeros((w.n_tokens, w.hidden)))
+    with pytest.raises(ValueError, match="GPU"):
+        lce.backward(hidden, shards, targets, lse, 1.0,
+                     d_shards=[torch.zeros((w.shard_rows, w.hidden)) for _ in range(w.n_shards)])
+    dims = lce.make_dims(w.n_tokens, w.hidden, w.vocab, w.n_shards)
+    with pytest.raises(ValueError, match="GPU"):
+        lce.fwd_round(dims, 0, 0, hidden, shards[0], targets, ws_host)
+    torch.cuda.synchronize()
