@@ -5,15 +5,16 @@
  * weight W (V x H) arrives as P column shards (contiguous vocabulary
  * intervals of V/P ids), and its gradients, without ever forming the N x V
  * logit tensor. This is one rank's share of the ring data-tensor-parallel
- * vocabulary projection described in "Flattening Every Memory Peak in
- * Long-Context Mixture-of-Experts Training", section 3.2 (Ring-DTP): the
- * rank's own batch meets every shard once, in the order a ring delivers them,
- * and each meeting folds the logits into a per-token running maximum and
- * exponential sum (the online-softmax update, Eq. 3 of that section); the
- * negative log-likelihood is m + log z - y_t. Backward recomputes each logit
- * block from the saved normalizer lse = m + log z. The same page requires the
- * operator to return the forward values and gradients of the plain
- * implementation, changing only the order of computation.
+ * vocabulary projection of "Flattening Every Memory Peak in Long-Context
+ * Mixture-of-Experts Training", section 3.2 (Ring-DTP). The rank's batch is
+ * multiplied by one shard after another, in ring delivery order; every
+ * product tile updates a per-token running maximum m and exponential sum z
+ * (online softmax, Eq. 3 of that section) and is then dropped. With
+ * lse_i = m_i + log z_i, token i's loss is lse_i - y_{t_i}. The backward
+ * rebuilds each logit tile from X, W and the stored lse (fp32, one value per
+ * token). Loss and gradients equal those of the plain full-logit
+ * cross-entropy up to floating-point rounding order (the exactness condition
+ * in the introduction to section 3).
  *
  * Conventions shared by every entry point:
  *  - Pointers marked "device" are HIP device pointers; "host" pointers are
@@ -91,7 +92,7 @@ typedef struct lce_dims {
 LCE_API size_t lce_workspace_bytes(const lce_dims* dims);
 
 /*
- * Forward: loss and the saved normalizer.
+ * Forward: loss and lse (the per-token log-sum-exp the backward reuses).
  *  hidden       device bf16 [N][H]
  *  w_shards     host array of P device pointers, each bf16 [V/P][H]
  *  shard_order  host int32 [P], a permutation of 0..P-1: round k meets shard
@@ -116,8 +117,8 @@ LCE_API int lce_forward(const lce_dims* dims, const void* hidden, const void* co
                 size_t workspace_bytes, void* stream);
 
 /*
- * Backward: gradients of the (mean or sum) loss, recomputed shard by shard
- * from the saved normalizer.
+ * Backward: gradients of the (mean or sum) loss; each shard's logit tiles
+ * are rebuilt from X, W and lse.
  *  hidden, w_shards, shard_order, targets   as for lce_forward
  *  lse          device fp32 [N] from lce_forward on the same inputs
  *  dloss        device fp32 scalar: d(objective)/d(loss); for

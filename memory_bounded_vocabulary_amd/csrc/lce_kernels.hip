@@ -2,11 +2,11 @@
 // cross-entropy, and the host-side launchers the C ABI calls.
 //
 // Method: "Flattening Every Memory Peak in Long-Context Mixture-of-Experts
-// Training", section 3.2 (Ring-DTP). Each round meets one vocabulary shard,
-// folds its logits into a per-token running (max, exp-sum) by the online
-// softmax update (Eq. 3), and never stores the logits; after the last round
-// the loss is m + log z - y_t. Backward recomputes each logit block from the
-// saved normalizer lse = m + log z.
+// Training", section 3.2 (Ring-DTP). One vocabulary shard per round; its
+// logit tiles update a per-token running (max m, exp-sum z) by the online
+// softmax rule (Eq. 3) and are never stored. loss_i = lse_i - y_{t_i} with
+// lse_i = m_i + log z_i; the backward rebuilds each logit tile from X, W and
+// the stored lse.
 #include <hip/hip_runtime.h>
 
 #include "lce_internal.hpp"

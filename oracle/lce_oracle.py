@@ -8,22 +8,23 @@ Everything here is plain float64 numpy on the host, written from:
 
 * "Flattening Every Memory Peak in Long-Context Mixture-of-Experts Training",
   section 3.2 (Ring-DTP; the section label is inferred, the extracted page has
-  no headings). A token's cross-entropy needs only a running maximum, an
-  exponential sum and its target logit; rank r owns a contiguous vocabulary
-  interval of size V/P (columns of the H x V projection weight); each round
-  forms one logit strip X W_r, folds it into the per-token state (m, z, y_t) by
-  the online-softmax update (Eq. 3, not reproduced by the extraction), and after
-  all P rounds the negative log-likelihood is m + log z - y_t. Backward
-  recomputes the strips from the saved normalizer.
-* The same page's exactness requirement (introduction to section 3): the
-  operator may change only the order of computation, so its forward values and
-  gradients must equal those of the plain implementation it replaces.
+  no headings). Per token the loss depends on three numbers only: the largest
+  logit, the sum of exponentials and the target's logit. Rank r holds one
+  contiguous block of V/P vocabulary ids (columns of the H x V projection
+  weight). A round multiplies the batch by one block and merges the resulting
+  strip into the per-token (m, z, y_t) with the online-softmax rule (Eq. 3,
+  missing from the extraction); at the end loss_i = m_i + log z_i - y_{t_i}.
+  The backward multiplies again, block by block, and needs only lse from the
+  forward.
+* The exactness condition in the introduction to section 3: the operator may
+  reorder the arithmetic but must produce the same loss and gradients as the
+  plain implementation.
 
 Because of that exactness requirement, ``cross_entropy`` below is the plain
 definition written out (full logit rows, two-pass stable log-sum-exp, textbook
 softmax-minus-one-hot gradient). ``ring_fold`` is the pages' algorithm in their
-order (strip by strip in ring order, online fold, then backward strip by strip
-from the saved normalizer); it exists so the tests can show the two agree.
+order (strip by strip in ring order, online fold, then the backward strip by
+strip from lse); it exists so the tests can show the two agree.
 
 Readings where the pages are silent (each also listed in the design notes):
 * Eq. 3 (missing) is read as the standard update m' = max(m, max_j y_j),

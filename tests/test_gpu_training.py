@@ -1,7 +1,7 @@
 """GPU parity of the training-loop extras: per-token upstream gradients
 (reduction "none"), bf16 gradient outputs, accumulation into existing
-gradients, and the recompute contract under activation checkpointing (the
-backward needs only the saved normalizer lse besides the inputs; "Flattening
+gradients, and the recompute contract under activation checkpointing (apart
+from the inputs the backward uses only lse from the forward; "Flattening
 Every Memory Peak in Long-Context Mixture-of-Experts Training", section 3.2).
 """
 import numpy as np
