@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the fused vocabulary projection + cross-entropy, forward + backward.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload small]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload stress]
 
 One step = lce_forward + lce_backward over one batch of the workload (all
 shards in ring order), inputs resident in HBM before the timed region. Prints
@@ -76,12 +76,18 @@ def cpu_baseline(batch, target_s: float):
             oracle.cross_entropy(x, wt, batch.targets[:n])
         return time.perf_counter() - t0
 
-    # calibrate on a few tokens, then take a prefix of the batch sized for
-    # about target_s seconds; if the whole batch takes less, repeat it
-    n_cal = max(8, min(w.n_tokens, int(2e10 / (6.0 * w.hidden * w.vocab))))
-    t_cal = run(n_cal)
-    n = int(min(w.n_tokens, max(n_cal, n_cal * target_s / max(t_cal, 1e-3))))
-    t = run(n) if n != n_cal else t_cal
+    # The oracle's cost is a fixed part (widening and zeroing the V x H
+    # gradient, which dominates at large V) plus a part linear in the tokens:
+    # time two prefixes to separate them, then take the prefix sized for about
+    # target_s seconds; if the whole batch takes less, repeat it.
+    n1 = max(8, min(w.n_tokens, int(2e10 / (6.0 * w.hidden * w.vocab))))
+    t1 = run(n1)
+    n2 = min(w.n_tokens, 4 * n1)
+    t2 = run(n2) if n2 > n1 else t1
+    slope = max((t2 - t1) / max(n2 - n1, 1), 1e-7)
+    fixed = max(0.0, t1 - slope * n1)
+    n = int(min(w.n_tokens, max(n2, (target_s - fixed) / slope)))
+    t = run(n) if n != n2 else t2
     reps = 1
     if n == w.n_tokens and t < 0.66 * target_s:
         reps = max(1, int(target_s / max(t, 1e-3)))
@@ -162,11 +168,13 @@ class ClockSampler:
             self._stop.wait(self.period)
 
     def __enter__(self):
+        self._t0 = time.perf_counter()
         if self._t:
             self._t.start()
         return self
 
     def __exit__(self, *exc):
+        self._window = time.perf_counter() - self._t0
         if self._t:
             self._stop.set()
             self._t.join()
@@ -175,8 +183,10 @@ class ClockSampler:
         if not self.samples:
             return None
         v = sorted(self.samples)
-        return {"source": "pp_dpm_sclk", "samples": len(v), "median_mhz": round(v[len(v) // 2], 1),
-                "min_mhz": round(v[0], 1), "max_mhz": round(v[-1], 1)}
+        # the driver's level is an average over a few milliseconds: meaningful
+        # for a window of about 100 ms or more
+        return {"source": "pp_dpm_sclk", "samples": len(v), "window_s": round(self._window, 2),
+                "median_mhz": round(v[len(v) // 2], 1), "min_mhz": round(v[0], 1), "max_mhz": round(v[-1], 1)}
 
 
 def _time_steps(fn, args, dev):
@@ -293,7 +303,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="small")
+    ap.add_argument("--workload", default="stress",
+                    help="workload name (default: stress, the largest one that fits one GPU)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
