@@ -117,6 +117,28 @@ LCE_API int lce_forward(const lce_dims* dims, const void* hidden, const void* co
                 size_t workspace_bytes, void* stream);
 
 /*
+ * Forward without a caller workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). Same arguments, kernels and results as lce_forward (bit
+ * for bit), but the forward's scratch (per-token split states, target logits,
+ * loss partials: the first part of lce_workspace_bytes) comes from a
+ * fixed-size device array built into the library, one copy per GPU, held
+ * until the process ends; lce_forward_noalloc_max_bytes() gives its size
+ * (32 MiB: N up to about 250 000 tokens). The call allocates nothing: the
+ * array's device address is looked up once per device, on the first call with
+ * that device current (the stream must belong to the current device).
+ * Returns LCE_ERR_WORKSPACE, enqueuing nothing, when the batch needs more
+ * scratch than the array holds. Every call on one GPU shares that GPU's
+ * array: calls that overlap on one GPU (two streams, or two threads) race and
+ * must be ordered by the caller. Nothing in the array needs to start at zero:
+ * each call writes what it reads.
+ */
+LCE_API int lce_forward_noalloc(const lce_dims* dims, const void* hidden, const void* const* w_shards,
+                                const int32_t* shard_order, const int32_t* targets, float* loss, float* lse,
+                                float* token_loss, void* stream);
+LCE_API size_t lce_forward_noalloc_max_bytes(void);
+
+/*
  * Backward: gradients of the (mean or sum) loss; each shard's logit tiles
  * are rebuilt from X, W and lse.
  *  hidden, w_shards, shard_order, targets   as for lce_forward

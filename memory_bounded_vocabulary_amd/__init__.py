@@ -24,9 +24,9 @@ LIB_PATH = os.path.join(HERE, "liblce.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 REDUCTIONS = {"mean": 0, "sum": 1, "none": 2}
 FLAG_ACCUMULATE_DX, FLAG_ACCUMULATE_DW, FLAG_BF16_GRADS = 1, 2, 4
-EXPORTED = ("lce_workspace_bytes", "lce_forward", "lce_backward", "lce_state_bytes", "lce_ring_payload",
-            "lce_fwd_round", "lce_fwd_finish", "lce_bwd_round", "lce_trace_enable", "lce_trace_collect", "lce_status_string", "lce_last_error",
-            "lce_version")
+EXPORTED = ("lce_workspace_bytes", "lce_forward", "lce_forward_noalloc", "lce_forward_noalloc_max_bytes",
+            "lce_backward", "lce_state_bytes", "lce_ring_payload", "lce_fwd_round", "lce_fwd_finish", "lce_bwd_round",
+            "lce_trace_enable", "lce_trace_collect", "lce_status_string", "lce_last_error", "lce_version")
 
 
 class Dims(ctypes.Structure):
@@ -64,6 +64,10 @@ def lib() -> ctypes.CDLL:
     L.lce_workspace_bytes.restype = ctypes.c_size_t
     L.lce_forward.argtypes = [dimp, vp, ctypes.POINTER(vp), i32p, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.lce_forward.restype = ctypes.c_int
+    L.lce_forward_noalloc.argtypes = [dimp, vp, ctypes.POINTER(vp), i32p, vp, vp, vp, vp, vp]
+    L.lce_forward_noalloc.restype = ctypes.c_int
+    L.lce_forward_noalloc_max_bytes.argtypes = []
+    L.lce_forward_noalloc_max_bytes.restype = ctypes.c_size_t
     L.lce_backward.argtypes = [dimp, vp, ctypes.POINTER(vp), i32p, vp, vp, vp, vp, ctypes.POINTER(vp), vp,
                                ctypes.c_size_t, vp]
     L.lce_backward.restype = ctypes.c_int
@@ -201,6 +205,27 @@ def forward(hidden, shards: Sequence, targets, ignore_index: int = -100, order: 
                            _nbytes(workspace), _stream(stream))
     _check(st)
     return (loss, lse, tl) if token_loss else (loss, lse)
+
+
+def forward_noalloc(hidden, shards: Sequence, targets, loss, lse, token_loss=None, ignore_index: int = -100,
+                    order: Optional[Sequence[int]] = None, reduction: str = "mean", stream=None) -> None:
+    """lce_forward_noalloc: the forward into caller-given outputs (loss fp32 [],
+    lse fp32 [N], token_loss fp32 [N] or None), with the library's built-in
+    scratch instead of a workspace; allocates nothing."""
+    import torch
+    _check_inputs(hidden, shards, targets, lse)
+    n = hidden.shape[0]
+    if loss.dtype != torch.float32 or loss.numel() != 1:
+        raise ValueError("loss must be a one-element fp32 tensor")
+    if token_loss is not None and (token_loss.dtype != torch.float32 or tuple(token_loss.shape) != (n,) or
+                                   not token_loss.is_contiguous()):
+        raise ValueError("token_loss must be a contiguous fp32 [N] tensor")
+    _require_cuda(hidden, targets, loss, lse, *shards, *([token_loss] if token_loss is not None else []))
+    p = len(shards)
+    d = make_dims(n, hidden.shape[1], p * shards[0].shape[0], p, ignore_index, reduction)
+    _check(lib().lce_forward_noalloc(ctypes.byref(d), hidden.data_ptr(), _ptr_array([s.data_ptr() for s in shards]),
+                                     _order_array(order), targets.data_ptr(), loss.data_ptr(), lse.data_ptr(),
+                                     token_loss.data_ptr() if token_loss is not None else None, _stream(stream)))
 
 
 def backward(hidden, shards: Sequence, targets, lse, dloss, ignore_index: int = -100,

@@ -21,6 +21,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -493,32 +494,45 @@ int lce_ring_payload(const lce_dims* d, size_t* weight_bytes, size_t* activation
   return x < w ? LCE_PAYLOAD_ACTIVATIONS : LCE_PAYLOAD_WEIGHTS;
 }
 
-int lce_forward(const lce_dims* d, const void* hidden, const void* const* w_shards, const int32_t* shard_order,
-                const int32_t* targets, float* loss, float* lse, float* token_loss, void* workspace,
-                size_t workspace_bytes, void* stream) {
-  Plan p;
-  int st = check_common(d, hidden, w_shards, targets, workspace, workspace_bytes, &p);
+}  // extern "C"
+
+namespace {
+
+// Argument checks of the forward that do not involve the workspace.
+int check_forward(const lce_dims* d, const void* hidden, const void* const* w_shards, const int32_t* shard_order,
+                  const int32_t* targets, float* loss, float* lse, float* token_loss, int32_t* order, Plan* p) {
+  int st = check_dims(d);
   if (st) return st;
+  if (!w_shards || (d->n_tokens > 0 && (!hidden || !targets)))
+    return fail(LCE_ERR_INVALID_ARG, "hidden, w_shards and targets must be non-NULL");
+  for (int s = 0; s < d->n_shards; ++s) {
+    if (!w_shards[s]) return fail(LCE_ERR_INVALID_ARG, "w_shards[%d] is NULL", s);
+    if (!aligned16(w_shards[s])) return fail(LCE_ERR_UNSUPPORTED, "w_shards[%d] is not 16-byte aligned", s);
+  }
+  if (!aligned16(hidden) || !aligned16(targets)) return fail(LCE_ERR_UNSUPPORTED, "hidden/targets not 16-byte aligned");
   if (!loss || (d->n_tokens > 0 && !lse)) return fail(LCE_ERR_INVALID_ARG, "loss and lse must be non-NULL");
   if (d->n_tokens > 0 && !token_loss && d->reduction == LCE_REDUCTION_NONE)
     return fail(LCE_ERR_INVALID_ARG, "token_loss must be non-NULL for LCE_REDUCTION_NONE");
   if (!aligned16(lse) || (token_loss && !aligned16(token_loss)))
     return fail(LCE_ERR_UNSUPPORTED, "lse/token_loss not 16-byte aligned");
-  int32_t order[LCE_MAX_SHARDS];
   st = check_order(shard_order, d->n_shards, order);
   if (st) return st;
-  g_last_error.clear();
+  *p = make_plan(d);
+  return LCE_OK;
+}
 
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+// The forward schedule on a checked workspace of at least p.fwd_bytes.
+int run_forward(const Plan& p, const lce_dims* d, const void* hidden, const void* const* w_shards,
+                const int32_t* order, const int32_t* targets, float* loss, float* lse, float* token_loss, char* ws,
+                hipStream_t s) {
   if (d->n_tokens == 0) return run_empty_loss(d, loss, s);
-  char* ws = static_cast<char*>(workspace);
   lce::ShardTable by_id{}, by_round{};
   for (int k = 0; k < d->n_shards; ++k) {
     by_id.p[k] = static_cast<const uint16_t*>(w_shards[k]);
     by_round.p[k] = static_cast<const uint16_t*>(w_shards[order[k]]);
   }
   const lce::FwdArgs a = fwd_args(p, d, hidden, targets, ws, loss, lse, token_loss);
-  st = run_target_logit(p, a, by_id, 0, d->n_shards, 1, s);
+  int st = run_target_logit(p, a, by_id, 0, d->n_shards, 1, s);
   if (st) return st;
   // All rounds in one launch when every workgroup is resident at once (its
   // state then stays in registers); else one launch per round.
@@ -530,6 +544,81 @@ int lce_forward(const lce_dims* d, const void* hidden, const void* const* w_shar
     if (st) return st;
   }
   return run_finalize(p, a, s);
+}
+
+// ---- the forward without a caller workspace --------------------------------
+// For callers that cannot allocate device memory: the forward's scratch (split
+// states, target logits, loss partials) lives in this file-scope array, one
+// copy per GPU, held until the process ends. In host code `scratch` is only a
+// stand-in for the symbol: its device address comes from hipGetSymbolAddress,
+// fetched once per device (with that device current) and kept in
+// g_scratch_addr; only that address ever reaches a kernel.
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+int static_scratch(void** out) {
+  int dev = -1;
+  int st = hip_status(hipGetDevice(&dev), "hipGetDevice");
+  if (st) return st;
+  if (dev < 0 || dev >= kMaxDevices) return fail(LCE_ERR_UNSUPPORTED, "device %d is beyond the %d supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* addr = nullptr;
+    st = hip_status(hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (st) return st;
+    if (!addr) return fail(LCE_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_addr[dev] = addr;
+  }
+  *out = g_scratch_addr[dev];
+  return LCE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lce_forward(const lce_dims* d, const void* hidden, const void* const* w_shards, const int32_t* shard_order,
+                const int32_t* targets, float* loss, float* lse, float* token_loss, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  Plan p;
+  int32_t order[LCE_MAX_SHARDS];
+  int st = check_forward(d, hidden, w_shards, shard_order, targets, loss, lse, token_loss, order, &p);
+  if (st) return st;
+  if (!workspace) return fail(LCE_ERR_INVALID_ARG, "workspace is NULL");
+  if (!aligned16(workspace)) return fail(LCE_ERR_UNSUPPORTED, "workspace is not 16-byte aligned");
+  if (workspace_bytes < p.bytes) return fail(LCE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, p.bytes);
+  g_last_error.clear();
+  return run_forward(p, d, hidden, w_shards, order, targets, loss, lse, token_loss, static_cast<char*>(workspace),
+                     reinterpret_cast<hipStream_t>(stream));
+}
+
+size_t lce_forward_noalloc_max_bytes(void) { return kStaticScratchBytes; }
+
+int lce_forward_noalloc(const lce_dims* d, const void* hidden, const void* const* w_shards, const int32_t* shard_order,
+                        const int32_t* targets, float* loss, float* lse, float* token_loss, void* stream) {
+  Plan p;
+  int32_t order[LCE_MAX_SHARDS];
+  int st = check_forward(d, hidden, w_shards, shard_order, targets, loss, lse, token_loss, order, &p);
+  if (st) return st;
+  if (p.fwd_bytes > kStaticScratchBytes)
+    return fail(LCE_ERR_WORKSPACE,
+                "the forward needs %zu bytes of scratch for N=%lld (%lld splits); the built-in scratch holds %zu",
+                p.fwd_bytes, (long long)p.N, (long long)p.splits, kStaticScratchBytes);
+  void* ws = nullptr;
+  st = static_scratch(&ws);
+  if (st) return st;
+  g_last_error.clear();
+  return run_forward(p, d, hidden, w_shards, order, targets, loss, lse, token_loss, static_cast<char*>(ws),
+                     reinterpret_cast<hipStream_t>(stream));
 }
 
 int lce_backward(const lce_dims* d, const void* hidden, const void* const* w_shards, const int32_t* shard_order,
@@ -717,6 +806,6 @@ const char* lce_status_string(int status) {
 
 const char* lce_last_error(void) { return g_last_error.c_str(); }
 
-int lce_version(void) { return (1 << 16) | 1; }
+int lce_version(void) { return (1 << 16) | 2; }
 
 }  // extern "C"

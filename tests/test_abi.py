@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     L = lce.lib()
     for name in declared_symbols():
         assert hasattr(L, name), name
-    assert lce.version() == (1, 1)
+    assert lce.version() == (1, 2)
 
 
 def test_single_hip_runtime_in_process():
@@ -374,3 +374,19 @@ def test_binding_round_calls_check_dims_against_tensors():
         lce.fwd_finish(dims, t, ws)
     with pytest.raises(ValueError, match="GPU"):
         lce.backward(x, [w, w], t, lse, torch.ones((n,)))
+
+
+def test_noalloc_forward_refuses_a_batch_beyond_its_scratch():
+    """lce_forward_noalloc checks the forward's scratch size on the host before
+    any GPU work (N = 2^19 tokens with 8 vocabulary splits need 34 MiB)."""
+    L = lce.lib()
+    assert L.lce_forward_noalloc_max_bytes() == 32 << 20
+    d = lce.make_dims(1 << 19, 64, 16 * 2048, 16)
+    arr = (ctypes.c_void_p * 16)(*([FAKE] * 16))
+    st = L.lce_forward_noalloc(ctypes.byref(d), FAKE, arr, None, FAKE, FAKE, FAKE, None, None)
+    assert st == lce.ERR_WORKSPACE
+    assert "scratch" in L.lce_last_error().decode()
+    # argument checks come first, as in lce_forward
+    assert L.lce_forward_noalloc(ctypes.byref(d), None, arr, None, FAKE, FAKE, FAKE, None, None) == lce.ERR_INVALID_ARG
+    assert L.lce_forward_noalloc(ctypes.byref(_dims(h=100)), FAKE, arr, None, FAKE, FAKE, FAKE, None, None) == \
+        lce.ERR_UNSUPPORTED
