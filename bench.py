@@ -76,20 +76,20 @@ def cpu_baseline(batch, target_s: float):
             oracle.cross_entropy(x, wt, batch.targets[:n])
         return time.perf_counter() - t0
 
-    # The oracle's cost is a fixed part (widening and zeroing the V x H
-    # gradient, which dominates at large V) plus a part linear in the tokens:
-    # time two prefixes to separate them, then take the prefix sized for about
-    # target_s seconds; if the whole batch takes less, repeat it.
-    n1 = max(8, min(w.n_tokens, int(2e10 / (6.0 * w.hidden * w.vocab))))
-    t1 = run(n1)
-    n2 = min(w.n_tokens, 4 * n1)
-    t2 = run(n2) if n2 > n1 else t1
-    slope = max((t2 - t1) / max(n2 - n1, 1), 1e-7)
-    fixed = max(0.0, t1 - slope * n1)
-    n = int(min(w.n_tokens, max(n2, (target_s - fixed) / slope)))
-    t = run(n) if n != n2 else t2
+    # The oracle works in blocks of rows, and each block pays a pass over the
+    # V x H gradient whatever its row count, so the sample starts at one full
+    # block of rows; it grows geometrically, at most 4x per run, until one run
+    # takes about half the target; if the whole batch takes less than that,
+    # it is repeated.
+    n = max(8, min(w.n_tokens, (1 << 26) // w.vocab))
+    t = run(n)
+    print(f"[bench] oracle sample: {n} tokens in {t:.1f} s", file=sys.stderr, flush=True)
+    while n < w.n_tokens and t < 0.5 * target_s:
+        n = min(w.n_tokens, int(n * min(4.0, max(1.5, 0.8 * target_s / max(t, 1e-3)))))
+        t = run(n)
+        print(f"[bench] oracle sample: {n} tokens in {t:.1f} s", file=sys.stderr, flush=True)
     reps = 1
-    if n == w.n_tokens and t < 0.66 * target_s:
+    if n == w.n_tokens and t < 0.5 * target_s:
         reps = max(1, int(target_s / max(t, 1e-3)))
         t = run(n, reps)
     cpu = "unknown"
