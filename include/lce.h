@@ -67,6 +67,11 @@ extern "C" {
 #define LCE_FLAG_ACCUMULATE_DW 2 /* backward adds into the shard gradients */
 #define LCE_FLAG_BF16_GRADS 4    /* d_hidden and the shard gradients are bf16 (accumulated
                                     in fp32 inside the workspace, rounded once at the end) */
+#define LCE_FLAG_KEEP_IGNORED_ROWS 8 /* the backward runs over every token, ignored ones
+                                        included (their gradient rows are zero either way):
+                                        no gathered copy of the hidden rows in the workspace,
+                                        so less memory, and more time when ignored tokens
+                                        would have saved a 256-token tile */
 
 #define LCE_MAX_SHARDS 256
 
@@ -83,10 +88,14 @@ typedef struct lce_dims {
 /*
  * Bytes of device workspace lce_forward and lce_backward need for `dims`.
  * Pure host function. The size is bounded independently of V: it holds
- * per-token state (O(N)) and two gradient chunks of at most 16384 x 8192 bf16
- * (fixed-size, whatever N and V), never a logit strip; with
+ * per-token state (O(N)), a bf16 copy of hidden rows whose target is not
+ * ignore_index (the backward leaves ignored tokens out when that saves a
+ * 256-token tile; at most N x H, or two token chunks of rows when that is
+ * less; none with LCE_FLAG_KEEP_IGNORED_ROWS) and two gradient chunks of at
+ * most 2^27 bf16 elements each (fixed-size, whatever N and V), never a logit
+ * strip; with
  * LCE_FLAG_BF16_GRADS also fp32 accumulators for d_hidden (N x H) and one
- * gradient chunk (at most 8192 x H).
+ * gradient chunk (at most 16384 x H).
  * Returns 0 if dims is invalid.
  */
 LCE_API size_t lce_workspace_bytes(const lce_dims* dims);
@@ -110,7 +119,11 @@ LCE_API size_t lce_workspace_bytes(const lce_dims* dims);
  *               lce_backward: it is the only state backward needs.
  *  token_loss   device fp32 [N] or NULL (required for LCE_REDUCTION_NONE);
  *               written: lse - target logit, 0 for ignored tokens.
- *  workspace    device buffer of at least lce_workspace_bytes(dims) bytes.
+ *  workspace    device buffer of at least lce_workspace_bytes(dims) bytes
+ *               (the size both passes need); the forward itself uses and
+ *               checks only its leading part, lce_state_bytes(dims) of dims
+ *               without flags, so one workspace sized for a backward with
+ *               any flags serves it.
  */
 LCE_API int lce_forward(const lce_dims* dims, const void* hidden, const void* const* w_shards, const int32_t* shard_order,
                 const int32_t* targets, float* loss, float* lse, float* token_loss, void* workspace,
@@ -254,7 +267,10 @@ LCE_API int lce_bwd_round(const lce_dims* dims, int round, int shard_index, cons
  * returns how many kinds it saw (or a negative status); it then empties the
  * trace for reuse. Entries also carry the launches' algorithmic work: MFMA
  * flops (2 x M x N x K of each contraction) and the bytes the kernel must move
- * at minimum (each operand read once, each output written once).
+ * at minimum (each operand read once, each output written once). Backward
+ * launches count the tokens the backward ran over: when it left ignored
+ * tokens out, only the others (the count is read back from the workspace of
+ * the last backward that used it).
  */
 typedef struct lce_trace_entry {
   char name[32];    /* kernel kind, e.g. "fwd_round", "gemm_dx" */

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(HERE, "liblce.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 REDUCTIONS = {"mean": 0, "sum": 1, "none": 2}
-FLAG_ACCUMULATE_DX, FLAG_ACCUMULATE_DW, FLAG_BF16_GRADS = 1, 2, 4
+FLAG_ACCUMULATE_DX, FLAG_ACCUMULATE_DW, FLAG_BF16_GRADS, FLAG_KEEP_IGNORED_ROWS = 1, 2, 4, 8
 EXPORTED = ("lce_workspace_bytes", "lce_forward", "lce_forward_noalloc", "lce_forward_noalloc_max_bytes",
             "lce_backward", "lce_state_bytes", "lce_ring_payload", "lce_fwd_round", "lce_fwd_finish", "lce_bwd_round",
             "lce_trace_enable", "lce_trace_collect", "lce_status_string", "lce_last_error", "lce_version")
@@ -231,12 +231,14 @@ def forward_noalloc(hidden, shards: Sequence, targets, loss, lse, token_loss=Non
 def backward(hidden, shards: Sequence, targets, lse, dloss, ignore_index: int = -100,
              order: Optional[Sequence[int]] = None, reduction: str = "mean", workspace=None,
              d_hidden=None, d_shards: Optional[List] = None, accumulate: bool = False,
-             grad_dtype=None, stream=None) -> Tuple[object, List]:
+             grad_dtype=None, keep_ignored_rows: bool = False, stream=None) -> Tuple[object, List]:
     """Gradients (d_hidden [N][H], [d_shard [V/P][H]]) of the loss scaled by dloss.
 
     dloss: scalar (mean / sum) or fp32 [N] (reduction "none"). grad_dtype:
     torch.float32 (default) or torch.bfloat16 (accumulated in fp32, rounded
-    once). accumulate: add into the given d_hidden / d_shards."""
+    once). accumulate: add into the given d_hidden / d_shards.
+    keep_ignored_rows: run over every token (no gathered copy of the hidden
+    rows in the workspace: less memory, same results)."""
     import torch
     _check_inputs(hidden, shards, targets, lse)
     _require_cuda(hidden, targets, lse, *shards)
@@ -251,6 +253,8 @@ def backward(hidden, shards: Sequence, targets, lse, dloss, ignore_index: int = 
         if d_hidden is None or d_shards is None:
             raise ValueError("accumulate needs the d_hidden and d_shards to add into")
         flags |= FLAG_ACCUMULATE_DX | FLAG_ACCUMULATE_DW
+    if keep_ignored_rows:
+        flags |= FLAG_KEEP_IGNORED_ROWS
     d = make_dims(n, h, p * vs, p, ignore_index, reduction, flags)
     if workspace is None:
         workspace = alloc_workspace(n, h, p * vs, p, hidden.device, ignore_index, reduction, flags)

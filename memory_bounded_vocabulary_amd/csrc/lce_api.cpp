@@ -31,11 +31,12 @@
 namespace {
 
 constexpr int64_t kTile = 256;
-constexpr int64_t kVocabChunkMax = 8192;   // vocabulary rows per backward chunk
-constexpr int64_t kTokenChunkMax = 16384;  // tokens per backward chunk
+constexpr int64_t kGChunkElems = int64_t(1) << 27;  // bf16 elements of one G chunk (256 MiB)
+constexpr int64_t kVocabChunkMax = 16384;           // vocabulary rows per backward chunk
 constexpr int kMaxSplits = 16;             // forward vocabulary splits per shard
 constexpr int kTargetWorkgroups = 256;     // one per compute unit
-constexpr int kKnownFlags = LCE_FLAG_ACCUMULATE_DX | LCE_FLAG_ACCUMULATE_DW | LCE_FLAG_BF16_GRADS;
+constexpr int kKnownFlags =
+    LCE_FLAG_ACCUMULATE_DX | LCE_FLAG_ACCUMULATE_DW | LCE_FLAG_BF16_GRADS | LCE_FLAG_KEEP_IGNORED_ROWS;
 
 thread_local std::string g_last_error;
 
@@ -63,7 +64,9 @@ struct Plan {
   // forward workspace
   size_t off_state, off_yt, off_part, fwd_bytes;
   // backward workspace (off_dx32 / off_dw32: fp32 accumulators for bf16 gradients)
-  size_t off_gscale, off_g, g_bytes, off_dx32, off_dw32, bwd_bytes;
+  size_t off_prep, off_tinfo, off_xv, xv_bytes, off_g, g_bytes, off_dx32, off_dw32, bwd_bytes;
+  bool xv_whole;  // the gathered hidden rows: all positions at once, or two token chunks
+  bool compact;   // the backward may leave ignored tokens out
   size_t state_bytes;  // leading bytes that carry state from one call of a sequence to the next
   bool bf16_grads;
   size_t bytes;
@@ -109,10 +112,36 @@ Plan make_plan(const lce_dims* d) {
       {kMaxSplits, p.vocab_tiles, std::max<int64_t>(8, ceil_div(kTargetWorkgroups, std::max<int64_t>(1, p.token_blocks)))});
   p.tiles_per_split = ceil_div(p.vocab_tiles, s);
   p.splits = ceil_div(p.vocab_tiles, p.tiles_per_split);
-  // Backward chunks: balanced, tile-aligned, bounded by constants.
+  // Backward chunks (vocabulary rows vc x tokens nc): tile-aligned, balanced,
+  // nc * vc within the G-chunk budget and vc within kVocabChunkMax, so the
+  // workspace does not grow with V. Each vocabulary chunk reads and writes
+  // the whole fp32 dX once, each token chunk after the first the shard's
+  // whole fp32 dW: among the admissible shapes take the one that moves the
+  // fewest such bytes, preferring fewer token chunks within 2 %.
   p.vs_pad = round_up(p.Vs, kTile);
-  p.vcs = round_up(ceil_div(p.vs_pad, ceil_div(p.vs_pad, kVocabChunkMax)), kTile);
-  p.ncs = p.n_pad ? round_up(ceil_div(p.n_pad, ceil_div(p.n_pad, kTokenChunkMax)), kTile) : 0;
+  p.vcs = std::min(p.vs_pad, kVocabChunkMax);
+  p.ncs = p.n_pad;
+  if (p.n_pad > 0) {
+    struct Shape { int64_t vc, nc, ct; double bytes; };
+    std::vector<Shape> shapes;
+    const double dx_pass = 8.0 * double(p.N) * double(p.H), dw_pass = 8.0 * double(p.V) * double(p.H);
+    for (int64_t cv = ceil_div(p.vs_pad, kVocabChunkMax); cv <= p.vs_pad / kTile; ++cv) {
+      const int64_t vc = round_up(ceil_div(p.vs_pad, cv), kTile);
+      const int64_t nc_max = kGChunkElems / vc / kTile * kTile;
+      if (nc_max < kTile) continue;
+      const int64_t ct = ceil_div(p.n_pad, nc_max);
+      const int64_t nc = round_up(ceil_div(p.n_pad, ct), kTile);
+      shapes.push_back({vc, nc, ct, double(p.P * ceil_div(p.vs_pad, vc)) * dx_pass + double(ct - 1) * dw_pass});
+    }
+    double best = shapes[0].bytes;
+    for (const Shape& sh : shapes) best = std::min(best, sh.bytes);
+    const Shape* pick = nullptr;
+    for (const Shape& sh : shapes)
+      if (sh.bytes <= 1.02 * best && (!pick || sh.ct < pick->ct || (sh.ct == pick->ct && sh.bytes < pick->bytes)))
+        pick = &sh;
+    p.vcs = pick->vc;
+    p.ncs = pick->nc;
+  }
 
   size_t o = 0;
   p.off_state = o;
@@ -134,8 +163,18 @@ Plan make_plan(const lce_dims* d) {
     o = align256(o + size_t(p.N) * p.H * 4);
   }
   const size_t bwd_state = o;
-  p.off_gscale = o;
-  o = align256(o + 16);
+  p.off_prep = o;  // BwdPrep
+  o = align256(o + sizeof(lce::BwdPrep));
+  p.off_tinfo = o;  // TokInfo per position
+  o = align256(o + size_t(p.n_pad) * sizeof(lce::TokInfo));
+  // hidden rows of the kept tokens (compact mode): all of them when that is
+  // no more than two token chunks, else two token-chunk buffers that the
+  // units' chunks alternate in
+  p.compact = (d->flags & LCE_FLAG_KEEP_IGNORED_ROWS) == 0;
+  p.xv_whole = p.N <= 2 * p.ncs;
+  p.xv_bytes = !p.compact ? 0 : p.xv_whole ? size_t(p.N) * p.H * 2 : align256(size_t(p.ncs) * p.H * 2);
+  p.off_xv = o;
+  o = align256(o + (p.xv_whole ? 1 : 2) * p.xv_bytes);
   p.g_bytes = align256(size_t(p.ncs) * p.vcs * 2);
   p.off_g = o;  // two G chunks: consecutive backward units alternate
   o += 2 * p.g_bytes;
@@ -190,15 +229,28 @@ int hip_status(hipError_t e, const char* what) {
 }
 
 // ---- optional per-launch event trace (see lce_trace_enable) ----
-enum Kind { kTargetLogit, kFwdRound, kFinalize, kBwdScale, kBwdG, kBwdStep, kGradGemm, kConvert, kKinds };
-const char* const kKindName[kKinds] = {"target_logit", "fwd_round", "finalize", "bwd_scale", "bwd_g", "bwd_step",
-                                       "grad_gemm",    "bf16_convert"};
+enum Kind { kTargetLogit, kFwdRound, kFinalize, kBwdPrep, kGather, kBwdG, kBwdStep, kGradGemm, kConvert, kKinds };
+const char* const kKindName[kKinds] = {"target_logit", "fwd_round", "finalize", "bwd_prep",     "gather",
+                                       "bwd_g",        "bwd_step",  "grad_gemm", "bf16_convert"};
+
+// Algorithmic work of one launch: a fixed part plus, for backward launches,
+// parts per position that exist (known on the device only: the positions of
+// a unit past the kept-token count do no work), read back when the trace is
+// collected.
+struct Work {
+  double flops = 0.0, bytes = 0.0;
+  const lce::BwdPrep* prep = nullptr;
+  int n0[2] = {0, 0}, nc[2] = {0, 0};
+  double flops_pp[2] = {0.0, 0.0}, bytes_pp[2] = {0.0, 0.0};
+  Work() = default;
+  Work(double f, double b) : flops(f), bytes(b) {}
+};
 
 struct Trace {
   std::vector<hipEvent_t> ev;  // pairs: [2i] before, [2i+1] after launch i
   struct Rec {
     int kind;
-    double flops, bytes;
+    Work work;
   };
   std::vector<Rec> recs;
   int64_t dropped[kKinds] = {};
@@ -206,7 +258,7 @@ struct Trace {
 thread_local Trace g_trace;
 
 template <class F>
-hipError_t traced(Kind kind, double flops, double bytes, hipStream_t s, F&& launch) {
+hipError_t traced(Kind kind, const Work& work, hipStream_t s, F&& launch) {
   Trace& t = g_trace;
   if (t.ev.empty()) return launch();
   const size_t i = t.recs.size();
@@ -220,7 +272,7 @@ hipError_t traced(Kind kind, double flops, double bytes, hipStream_t s, F&& laun
   if (e != hipSuccess) return e;
   e = hipEventRecord(t.ev[2 * i + 1], s);
   if (e != hipSuccess) return e;
-  t.recs.push_back({int(kind), flops, bytes});
+  t.recs.push_back({int(kind), work});
   return hipSuccess;
 }
 
@@ -254,7 +306,7 @@ lce::FwdArgs fwd_args(const Plan& p, const lce_dims* d, const void* hidden, cons
 int run_target_logit(const Plan& p, const lce::FwdArgs& a, const lce::ShardTable& by_id, int s_lo, int s_hi, int init,
                      hipStream_t s) {
   const double dN = double(p.N), dH = double(p.H);
-  return hip_status(traced(kTargetLogit, 0.0, 4.0 * dN * dH + 8.0 * dN, s,
+  return hip_status(traced(kTargetLogit, Work(0.0, 4.0 * dN * dH + 8.0 * dN), s,
                            [&] {
                              return lce::launch_target_logit(a.X, a.N, a.H, by_id, a.Vs, int(p.V), s_lo, s_hi,
                                                              a.targets, a.ignore_index, const_cast<float*>(a.yt), init,
@@ -270,17 +322,18 @@ int run_fwd_rounds(const Plan& p, const lce::FwdArgs& a, const lce::ShardTable& 
   const double flops = 2.0 * dN * dVs * dH * nr;
   const double bytes = 2.0 * dN * dH + 2.0 * dVs * dH * nr + (first ? 8.0 : 16.0) * dS * dN;
   return hip_status(
-      traced(kFwdRound, flops, bytes, s, [&] { return lce::launch_fwd_rounds(a, by_round, k0, k1, first, s); }),
+      traced(kFwdRound, Work(flops, bytes), s, [&] { return lce::launch_fwd_rounds(a, by_round, k0, k1, first, s); }),
       "forward rounds");
 }
 
 int run_finalize(const Plan& p, const lce::FwdArgs& a, hipStream_t s) {
-  return hip_status(traced(kFinalize, 0.0, 8.0 * double(p.splits) * double(p.N) + 16.0 * double(p.N), s,
+  return hip_status(traced(kFinalize, Work(0.0, 8.0 * double(p.splits) * double(p.N) + 16.0 * double(p.N)), s,
                            [&] { return lce::launch_finalize(a, s); }),
                     "finalize");
 }
 
 // One backward unit: a (vocabulary chunk, token chunk) block of one shard.
+// Token chunks are ranges of positions (see lce::BwdPrep).
 struct Unit {
   int sh, v0, vc, vc_pad, n0, nc, nc_pad;
   const uint16_t* W;  // the shard
@@ -290,54 +343,73 @@ struct Unit {
   bool chunk_first, chunk_last;  // first / last unit of its (shard, vocabulary chunk)
 };
 
-// The units of one shard, in order; acc_dx/acc_dw set from `dx_written`
-// (per token chunk: has dX been written yet in this backward) and `acc_dw`.
-void shard_units(const Plan& p, int sh, const uint16_t* W, void* dW_out, char* ws, std::vector<bool>& dx_written,
-                 bool acc_dw, std::vector<Unit>& out) {
-  for (int64_t v0 = 0; v0 < p.Vs; v0 += p.vcs) {
+// The units of the shards `ids` (in ring order). Each token chunk's first
+// unit writes dX (adds, with acc_dx), later ones add; each (shard, vocabulary
+// chunk)'s first token chunk writes its dW rows (adds, with acc_dw). With fp32
+// gradients the token chunk is the outer loop, so that each chunk's hidden
+// rows are gathered once; with bf16 gradients a (shard, vocabulary chunk) runs
+// all its token chunks back to back, for its one fp32 accumulator. Every dX
+// and dW element gets its terms in the same order either way (shards in ring
+// order for dX, token chunks in order for dW), so the results are equal.
+std::vector<Unit> backward_units(const Plan& p, const int32_t* ids, int n_ids, const void* const* w_by_id,
+                                 void* const* dw_by_id, char* ws, bool acc_dx, bool acc_dw) {
+  std::vector<Unit> out;
+  std::vector<bool> dx_written(size_t(ceil_div(p.N, p.ncs)), acc_dx);
+  auto add = [&](int k, int64_t v0, int64_t n0) {
+    const int sh = ids[k];
     const int vc = int(std::min<int64_t>(p.vcs, p.Vs - v0));
-    for (int64_t n0 = 0; n0 < p.N; n0 += p.ncs) {
-      const int nc = int(std::min<int64_t>(p.ncs, p.N - n0));
-      const size_t nchunk = size_t(n0 / p.ncs);
-      Unit u{sh, int(v0), vc, int(round_up(vc, kTile)), int(n0), nc, int(round_up(nc, kTile)), W,
-             nullptr, nullptr, 0, 0, n0 == 0, n0 + p.ncs >= p.N};
-      if (p.bf16_grads) {
-        u.dW = reinterpret_cast<float*>(ws + p.off_dw32);
-        u.dW_bf16 = static_cast<uint16_t*>(dW_out) + size_t(v0) * p.H;
-      } else {
-        u.dW = static_cast<float*>(dW_out) + size_t(v0) * p.H;
-      }
-      u.acc_dx = dx_written[nchunk] ? 1 : 0;
-      dx_written[nchunk] = true;
-      u.acc_dw = (acc_dw || n0 > 0) ? 1 : 0;
-      out.push_back(u);
+    const int nc = int(std::min<int64_t>(p.ncs, p.N - n0));
+    const size_t nchunk = size_t(n0 / p.ncs);
+    Unit u{sh, int(v0), vc, int(round_up(vc, kTile)), int(n0), nc, int(round_up(nc, kTile)),
+           static_cast<const uint16_t*>(w_by_id[k]), nullptr, nullptr, 0, 0, n0 == 0, n0 + p.ncs >= p.N};
+    if (p.bf16_grads) {
+      u.dW = reinterpret_cast<float*>(ws + p.off_dw32);
+      u.dW_bf16 = static_cast<uint16_t*>(dw_by_id[k]) + size_t(v0) * p.H;
+    } else {
+      u.dW = static_cast<float*>(dw_by_id[k]) + size_t(v0) * p.H;
     }
+    u.acc_dx = dx_written[nchunk] ? 1 : 0;
+    dx_written[nchunk] = true;
+    u.acc_dw = (acc_dw || n0 > 0) ? 1 : 0;
+    out.push_back(u);
+  };
+  if (p.bf16_grads) {
+    for (int k = 0; k < n_ids; ++k)
+      for (int64_t v0 = 0; v0 < p.Vs; v0 += p.vcs)
+        for (int64_t n0 = 0; n0 < p.N; n0 += p.ncs) add(k, v0, n0);
+  } else {
+    for (int64_t n0 = 0; n0 < p.N; n0 += p.ncs)
+      for (int k = 0; k < n_ids; ++k)
+        for (int64_t v0 = 0; v0 < p.Vs; v0 += p.vcs) add(k, v0, n0);
   }
+  return out;
 }
 
-// g = dloss / n_valid (mean) or dloss (sum) into the workspace; for
-// LCE_REDUCTION_NONE nothing runs and the per-token dloss is read directly.
-int run_bwd_scale(const Plan& p, const lce_dims* d, const int32_t* targets, const float* dloss, char* ws,
-                  const float** g, int* g_per_token, hipStream_t s) {
-  if (d->reduction == LCE_REDUCTION_NONE) {
-    *g = dloss;
-    *g_per_token = 1;
-    return LCE_OK;
-  }
-  float* gscale = reinterpret_cast<float*>(ws + p.off_gscale);
-  *g = gscale;
-  *g_per_token = 0;
-  return hip_status(traced(kBwdScale, 0.0, 4.0 * double(p.N), s,
+// Token info of the positions the backward runs over (kept tokens only when
+// that saves a token tile) and the loss scale; then, in compact mode, zero
+// the ignored rows of `dx_zero` (NULL: leave them, when accumulating).
+int run_bwd_prep(const Plan& p, const lce_dims* d, const int32_t* targets, const float* lse, const float* dloss,
+                 float* dx_zero, char* ws, hipStream_t s) {
+  lce::BwdPrep* prep = reinterpret_cast<lce::BwdPrep*>(ws + p.off_prep);
+  lce::TokInfo* tinfo = reinterpret_cast<lce::TokInfo*>(ws + p.off_tinfo);
+  int st = hip_status(traced(kBwdPrep, Work(0.0, 4.0 * double(p.N) + 16.0 * double(p.N)), s,
+                             [&] {
+                               return lce::launch_bwd_prep(targets, lse, int(p.N), d->ignore_index, dloss,
+                                                           d->reduction, p.compact ? 1 : 0, prep, tinfo, s);
+                             }),
+                      "backward preparation");
+  if (st || !dx_zero) return st;
+  return hip_status(traced(kGather, Work(0.0, 0.0), s,
                            [&] {
-                             return lce::launch_bwd_scale(targets, int(p.N), d->ignore_index, dloss, d->reduction,
-                                                          gscale, s);
+                             return lce::launch_zero_ignored_rows(dx_zero, prep, targets, int(p.N), int(p.H),
+                                                                  d->ignore_index, s);
                            }),
-                    "scale");
+                    "zero ignored rows");
 }
 
 int run_convert(bool widen, const void* src, void* dst, int64_t rows, int64_t cols, hipStream_t s) {
   const double n = double(rows) * double(cols);
-  return hip_status(traced(kConvert, 0.0, 6.0 * n, s,
+  return hip_status(traced(kConvert, Work(0.0, 6.0 * n), s,
                            [&] {
                              return widen ? lce::launch_widen_bf16(static_cast<const uint16_t*>(src),
                                                                    static_cast<float*>(dst), rows, cols, s)
@@ -351,22 +423,60 @@ int run_convert(bool widen, const void* src, void* dst, int64_t rows, int64_t co
 // With bf16 gradients each vocabulary chunk's dW accumulates in the chunk
 // accumulator and is narrowed into the caller's buffer after the launch that
 // ends it (and, when accumulating, widened from it before the launch that
-// starts it).
-int run_bwd_units(const Plan& p, const lce_dims* d, const std::vector<Unit>& units, const uint16_t* X,
-                  const int32_t* targets, const float* lse, const float* g, int g_per_token, float* dX, bool acc_dw,
-                  char* ws, hipStream_t s) {
+// starts it). In compact mode the units read their token chunk's hidden rows
+// from a gathered copy: all positions in one buffer when they fit
+// (xv_whole), else two chunk buffers; a unit whose chunk is not in a buffer
+// gets it gathered, before its recompute launch, into the buffer the
+// previous unit does not use (whose GEMMs run in that same launch).
+int run_bwd_units(const Plan& p, const lce_dims* d, const std::vector<Unit>& units, const uint16_t* X, float* dX,
+                  bool acc_dw, char* ws, hipStream_t s) {
   const double dH = double(p.H);
   auto gbuf = [&](size_t u) { return reinterpret_cast<uint16_t*>(ws + p.off_g + (u & 1) * p.g_bytes); };
   float* dw32 = reinterpret_cast<float*>(ws + p.off_dw32);
+  const lce::BwdPrep* prep = reinterpret_cast<const lce::BwdPrep*>(ws + p.off_prep);
+  const lce::TokInfo* tinfo = reinterpret_cast<const lce::TokInfo*>(ws + p.off_tinfo);
+  uint16_t* xv_base = reinterpret_cast<uint16_t*>(ws + p.off_xv);
+  auto gather = [&](uint16_t* dst, int n0, int nc) {
+    return hip_status(traced(kGather, Work(0.0, 4.0 * double(nc) * dH), s,
+                             [&] { return lce::launch_gather_rows(X, dst, prep, tinfo, n0, nc, int(p.H), s); }),
+                      "gather rows");
+  };
+  // the gathered rows of each unit's positions
+  std::vector<uint16_t*> xv(units.size());
+  std::vector<int> gather_before(units.size(), -1);  // launch j gathers unit j's chunk first
   int st;
+  if (!p.compact) {
+    for (size_t j = 0; j < units.size(); ++j) xv[j] = nullptr;  // the kernels read X
+  } else if (p.xv_whole) {
+    st = gather(xv_base, 0, int(p.N));
+    if (st) return st;
+    for (size_t j = 0; j < units.size(); ++j) xv[j] = xv_base + size_t(units[j].n0) * p.H;
+  } else {
+    int held[2] = {-1, -1}, prev = 1;
+    for (size_t j = 0; j < units.size(); ++j) {
+      int b = held[0] == units[j].n0 ? 0 : held[1] == units[j].n0 ? 1 : -1;
+      if (b < 0) {
+        b = prev ^ 1;
+        held[b] = units[j].n0;
+        gather_before[j] = b;
+      }
+      xv[j] = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(xv_base) + b * p.xv_bytes);
+      prev = b;
+    }
+  }
   if (!units.empty() && units[0].dW_bf16 && acc_dw) {
     st = run_convert(true, units[0].dW_bf16, dw32, units[0].vc, p.H, s);
     if (st) return st;
   }
   for (size_t j = 0; j <= units.size(); ++j) {
+    if (j < units.size() && gather_before[j] >= 0) {
+      st = gather(xv[j], units[j].n0, units[j].nc);
+      if (st) return st;
+    }
     lce::GradArgs ga{};
     lce::BwdGArgs ba{};
-    double flops = 0.0, bytes = 0.0;
+    Work work;
+    work.prep = prep;
     if (j > 0) {
       const Unit& u = units[j - 1];
       ga.G = gbuf(j - 1);
@@ -375,28 +485,34 @@ int run_bwd_units(const Plan& p, const lce_dims* d, const std::vector<Unit>& uni
       ga.vc_pad = u.vc_pad;
       ga.Wc = u.W + size_t(u.v0) * p.H;
       ga.vc = u.vc;
-      ga.Xc = X + size_t(u.n0) * p.H;
+      ga.X = X;
+      ga.xv = xv[j - 1];
+      ga.prep = prep;
+      ga.tinfo = tinfo;
+      ga.n0 = u.n0;
       ga.nc = u.nc;
       ga.H = int(p.H);
-      ga.dX = dX + size_t(u.n0) * p.H;
+      ga.dX = dX;
       ga.acc_dx = u.acc_dx;
       ga.dW = u.dW;
       ga.acc_dw = u.acc_dw;
-      const double dnc = u.nc, dvc = u.vc, gb = 2.0 * double(u.nc_pad) * double(u.vc_pad);
-      flops += 4.0 * dnc * dvc * dH;
-      bytes += 2.0 * gb + 2.0 * dvc * dH + 2.0 * dnc * dH + (4.0 + 4.0 * u.acc_dx) * dnc * dH +
-               (4.0 + 4.0 * u.acc_dw) * dvc * dH;
+      // per position: the two contractions, G read twice, the position's X
+      // row and dX row (read when adding); fixed: the W chunk, the dW rows
+      const double dvc = u.vc;
+      work.n0[0] = u.n0;
+      work.nc[0] = u.nc;
+      work.flops_pp[0] = 4.0 * dvc * dH;
+      work.bytes_pp[0] = 4.0 * double(u.vc_pad) + 2.0 * dH + (4.0 + 4.0 * u.acc_dx) * dH;
+      work.bytes += 2.0 * dvc * dH + (4.0 + 4.0 * u.acc_dw) * dvc * dH;
     }
     if (j < units.size()) {
       const Unit& u = units[j];
       ba.X = X;
+      ba.xv = xv[j];
+      ba.prep = prep;
+      ba.tinfo = tinfo;
       ba.Ws = u.W;
-      ba.targets = targets;
-      ba.lse = lse;
-      ba.gscale = g;
-      ba.g_per_token = g_per_token;
       ba.G = gbuf(j);
-      ba.N = int(p.N);
       ba.H = int(p.H);
       ba.Vs = int(p.Vs);
       ba.v0 = u.v0;
@@ -409,12 +525,17 @@ int run_bwd_units(const Plan& p, const lce_dims* d, const std::vector<Unit>& uni
       ba.vocab_base = int(u.sh * p.Vs + u.v0);
       ba.V = int(p.V);
       ba.ldg = u.vc_pad;
-      const double dnc = u.nc, dvc = u.vc;
-      flops += 2.0 * dnc * dvc * dH;
-      bytes += 2.0 * dnc * dH + 2.0 * dvc * dH + 2.0 * double(u.nc_pad) * double(u.vc_pad) + 12.0 * dnc;
+      // per position: the recompute, its X row, its G row, its token info;
+      // fixed: the W chunk
+      const double dvc = u.vc;
+      work.n0[1] = u.n0;
+      work.nc[1] = u.nc;
+      work.flops_pp[1] = 2.0 * dvc * dH;
+      work.bytes_pp[1] = 2.0 * dH + 2.0 * double(u.vc_pad) + 16.0;
+      work.bytes += 2.0 * dvc * dH;
     }
     const Kind kind = j == 0 ? kBwdG : (j == units.size() ? kGradGemm : kBwdStep);
-    st = hip_status(traced(kind, flops, bytes, s,
+    st = hip_status(traced(kind, work, s,
                            [&] {
                              return lce::launch_bwd_step(j > 0 ? &ga : nullptr, j < units.size() ? &ba : nullptr,
                                                          s);
@@ -437,12 +558,12 @@ int run_bwd_units(const Plan& p, const lce_dims* d, const std::vector<Unit>& uni
 // sum of none (0); a shard gradient is zero.
 int run_empty_loss(const lce_dims* d, float* loss, hipStream_t s) {
   const float v = d->reduction == LCE_REDUCTION_MEAN ? __builtin_nanf("") : 0.0f;
-  return hip_status(traced(kFinalize, 0.0, 4.0, s, [&] { return lce::launch_set_scalar(loss, v, s); }), "empty loss");
+  return hip_status(traced(kFinalize, Work(0.0, 4.0), s, [&] { return lce::launch_set_scalar(loss, v, s); }), "empty loss");
 }
 
 int run_zero(const Plan& p, void* d_w_shard, hipStream_t s) {
   const size_t bytes = size_t(p.Vs) * p.H * (p.bf16_grads ? 2 : 4);
-  return hip_status(traced(kConvert, 0.0, double(bytes), s, [&] { return lce::launch_zero(d_w_shard, bytes, s); }),
+  return hip_status(traced(kConvert, Work(0.0, double(bytes)), s, [&] { return lce::launch_zero(d_w_shard, bytes, s); }),
                     "zero gradient");
 }
 
@@ -595,7 +716,9 @@ int lce_forward(const lce_dims* d, const void* hidden, const void* const* w_shar
   if (st) return st;
   if (!workspace) return fail(LCE_ERR_INVALID_ARG, "workspace is NULL");
   if (!aligned16(workspace)) return fail(LCE_ERR_UNSUPPORTED, "workspace is not 16-byte aligned");
-  if (workspace_bytes < p.bytes) return fail(LCE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, p.bytes);
+  // the forward uses only its own leading part of the workspace
+  if (workspace_bytes < p.fwd_bytes)
+    return fail(LCE_ERR_WORKSPACE, "workspace has %zu bytes, the forward needs %zu", workspace_bytes, p.fwd_bytes);
   g_last_error.clear();
   return run_forward(p, d, hidden, w_shards, order, targets, loss, lse, token_loss, static_cast<char*>(workspace),
                      reinterpret_cast<hipStream_t>(stream));
@@ -649,22 +772,21 @@ int lce_backward(const lce_dims* d, const void* hidden, const void* const* w_sha
     }
     return LCE_OK;
   }
-  const float* g = nullptr;
-  int g_per_token = 0;
-  st = run_bwd_scale(p, d, targets, dloss, ws, &g, &g_per_token, s);
-  if (st) return st;
   float* dx32 = p.bf16_grads ? reinterpret_cast<float*>(ws + p.off_dx32) : static_cast<float*>(d_hidden);
   if (p.bf16_grads && acc_dx) {
     st = run_convert(true, d_hidden, dx32, p.N, p.H, s);
     if (st) return st;
   }
-  std::vector<Unit> units;
-  std::vector<bool> dx_written(size_t(ceil_div(p.N, p.ncs)), acc_dx);
-  for (int k = 0; k < d->n_shards; ++k)
-    shard_units(p, order[k], static_cast<const uint16_t*>(w_shards[order[k]]), d_w_shards[order[k]], ws, dx_written,
-                acc_dw, units);
-  st = run_bwd_units(p, d, units, static_cast<const uint16_t*>(hidden), targets, lse, g, g_per_token, dx32, acc_dw,
-                     ws, s);
+  st = run_bwd_prep(p, d, targets, lse, dloss, acc_dx ? nullptr : dx32, ws, s);
+  if (st) return st;
+  const void* w_by_round[LCE_MAX_SHARDS];
+  void* dw_by_round[LCE_MAX_SHARDS];
+  for (int k = 0; k < d->n_shards; ++k) {
+    w_by_round[k] = w_shards[order[k]];
+    dw_by_round[k] = d_w_shards[order[k]];
+  }
+  const std::vector<Unit> units = backward_units(p, order, d->n_shards, w_by_round, dw_by_round, ws, acc_dx, acc_dw);
+  st = run_bwd_units(p, d, units, static_cast<const uint16_t*>(hidden), dx32, acc_dw, ws, s);
   if (st || !p.bf16_grads) return st;
   return run_convert(false, dx32, d_hidden, p.N, p.H, s);
 }
@@ -722,20 +844,18 @@ int lce_bwd_round(const lce_dims* d, int round, int shard_index, const void* hid
   const bool acc_dx = round > 0 || (d->flags & LCE_FLAG_ACCUMULATE_DX) != 0;
   const bool acc_dw = accumulate_dw != 0 || (d->flags & LCE_FLAG_ACCUMULATE_DW) != 0;
   if (d->n_tokens == 0) return acc_dw ? LCE_OK : run_zero(p, d_w_shard, s);
-  const float* g = nullptr;
-  int g_per_token = 0;
-  st = run_bwd_scale(p, d, targets, dloss, ws, &g, &g_per_token, s);
-  if (st) return st;
   float* dx32 = p.bf16_grads ? reinterpret_cast<float*>(ws + p.off_dx32) : static_cast<float*>(d_hidden);
   if (p.bf16_grads && round == 0 && acc_dx) {
     st = run_convert(true, d_hidden, dx32, p.N, p.H, s);
     if (st) return st;
   }
-  std::vector<Unit> units;
-  std::vector<bool> dx_written(size_t(ceil_div(p.N, p.ncs)), acc_dx);
-  shard_units(p, shard_index, static_cast<const uint16_t*>(w_shard), d_w_shard, ws, dx_written, acc_dw, units);
-  st = run_bwd_units(p, d, units, static_cast<const uint16_t*>(hidden), targets, lse, g, g_per_token, dx32, acc_dw,
-                     ws, s);
+  st = run_bwd_prep(p, d, targets, lse, dloss, acc_dx ? nullptr : dx32, ws, s);
+  if (st) return st;
+  const int32_t id = shard_index;
+  const void* w_one[1] = {w_shard};
+  void* dw_one[1] = {d_w_shard};
+  const std::vector<Unit> units = backward_units(p, &id, 1, w_one, dw_one, ws, acc_dx, acc_dw);
+  st = run_bwd_units(p, d, units, static_cast<const uint16_t*>(hidden), dx32, acc_dw, ws, s);
   if (st || !p.bf16_grads || round != d->n_shards - 1) return st;
   return run_convert(false, dx32, d_hidden, p.N, p.H, s);
 }
@@ -772,15 +892,43 @@ int lce_trace_collect(lce_trace_entry* out, int max_entries) {
     int st = hip_status(hipEventSynchronize(t.ev[2 * t.recs.size() - 1]), "hipEventSynchronize");
     if (st) return st;
   }
+  // positions that exist, per backward preparation record (as it stands now:
+  // the last backward on that workspace)
+  std::vector<std::pair<const lce::BwdPrep*, int>> n_eff;
+  auto positions = [&](const lce::BwdPrep* prep, int* n) {
+    for (const auto& e : n_eff)
+      if (e.first == prep) {
+        *n = e.second;
+        return LCE_OK;
+      }
+    lce::BwdPrep host{};
+    int st = hip_status(hipMemcpy(&host, prep, sizeof host, hipMemcpyDeviceToHost), "hipMemcpy(trace)");
+    if (st) return st;
+    n_eff.push_back({prep, host.n_eff});
+    *n = host.n_eff;
+    return LCE_OK;
+  };
   for (size_t i = 0; i < t.recs.size(); ++i) {
     float ms = 0.0f;
     int st = hip_status(hipEventElapsedTime(&ms, t.ev[2 * i], t.ev[2 * i + 1]), "hipEventElapsedTime");
     if (st) return st;
+    const Work& w = t.recs[i].work;
+    double flops = w.flops, bytes = w.bytes;
+    if (w.prep) {
+      int n = 0;
+      st = positions(w.prep, &n);
+      if (st) return st;
+      for (int h = 0; h < 2; ++h) {
+        const double live = double(std::max(0, std::min(w.nc[h], n - w.n0[h])));
+        flops += w.flops_pp[h] * live;
+        bytes += w.bytes_pp[h] * live;
+      }
+    }
     lce_trace_entry& a = agg[t.recs[i].kind];
     a.launches += 1;
     a.total_ms += ms;
-    a.flops += t.recs[i].flops;
-    a.bytes += t.recs[i].bytes;
+    a.flops += flops;
+    a.bytes += bytes;
   }
   int n = 0;
   for (int k = 0; k < kKinds; ++k) {

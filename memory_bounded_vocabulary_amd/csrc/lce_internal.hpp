@@ -35,18 +35,49 @@ hipError_t launch_finalize(const FwdArgs& a, hipStream_t st);
 // (shards.p indexed by shard id); `init` first resets yt.
 hipError_t launch_target_logit(const uint16_t* X, int N, int H, const ShardTable& shards, int Vs, int V, int s_lo,
                                int s_hi, const int* targets, int ignore_index, float* yt, int init, hipStream_t st);
-hipError_t launch_bwd_scale(const int* targets, int N, int ignore_index, const float* dloss, int reduction,
-                            float* gscale, hipStream_t st);
+// Backward preparation, written on the device by launch_bwd_prep. Only
+// tokens whose target is not ignore_index can have a nonzero gradient row.
+// When leaving the ignored ones out saves at least one 256-token tile,
+// `compact` is set: the backward runs over the n_eff = n_valid kept tokens in
+// ascending order ("positions"), tinfo[0 .. n_eff) describes them, and
+// launch_gather_rows copies a range of their hidden rows into a buffer the
+// contractions read. Otherwise n_eff = N, position i is token i, and the
+// kernels read X itself.
+struct BwdPrep {
+  int n_valid;              // tokens with target != ignore_index
+  int n_eff;                // positions the backward runs over (n_valid or N)
+  int compact;              // 1: positions are the kept tokens only
+  float gscale;             // dloss / n_valid (mean) or dloss (sum)
+};
+// What the G formation needs of the token at one position.
+struct TokInfo {
+  float lse;                // from the forward
+  int target;
+  float g;                  // gscale (mean / sum) or the token's dloss (none)
+  int row;                  // the token's row in X, dX
+};
+// allow_compact = 0 keeps every token (no gathered copy exists then).
+hipError_t launch_bwd_prep(const int* targets, const float* lse, int N, int ignore_index, const float* dloss,
+                           int reduction, int allow_compact, BwdPrep* prep, TokInfo* tinfo, hipStream_t st);
+// Compact mode only (else it does nothing): xv[i] = X[tinfo[n0 + i].row] for
+// the positions n0 + i < min(n0 + nc, n_eff).
+hipError_t launch_gather_rows(const uint16_t* X, uint16_t* xv, const BwdPrep* prep, const TokInfo* tinfo, int n0,
+                              int nc, int H, hipStream_t st);
+// Compact mode only: zero the rows of dX [N][H] fp32 whose target is
+// ignore_index (the contractions never write them in compact mode).
+hipError_t launch_zero_ignored_rows(float* dX, const BwdPrep* prep, const int* targets, int N, int H,
+                                    int ignore_index, hipStream_t st);
 // Recompute + G of one backward unit (shard, vocabulary chunk, token chunk).
+// Token indices n0, nc are positions (see BwdPrep).
 struct BwdGArgs {
   const uint16_t* X;        // hidden [N][H]
+  const uint16_t* xv;       // compact mode: the hidden rows of positions n0 ..
+  const BwdPrep* prep;
+  const TokInfo* tinfo;
   const uint16_t* Ws;       // the unit's shard [Vs][H]
-  const int* targets;
-  const float* lse;
-  const float* gscale;      // g = dloss / n_valid (or dloss): gscale[0], or gscale[row] if g_per_token
   uint16_t* G;              // [nc_pad][vc_pad], pitch ldg
-  int N, H, Vs, v0, vc, n0, nc, nc_pad, vc_pad;
-  int ignore_index, vocab_base, V, ldg, g_per_token;
+  int H, Vs, v0, vc, n0, nc, nc_pad, vc_pad;
+  int ignore_index, vocab_base, V, ldg;
   int n_tt, n_tv;           // set by the launcher
 };
 
@@ -54,9 +85,13 @@ struct BwdGArgs {
 struct GradArgs {
   const uint16_t* G;        // [nc_pad][vc_pad], pitch ldg
   const uint16_t* Wc;       // shard rows v0.. [vc][H]
-  const uint16_t* Xc;       // hidden rows n0.. [nc][H]
-  float* dX;                // d_hidden rows n0..
+  const uint16_t* X;        // hidden [N][H]
+  const uint16_t* xv;       // compact mode: the hidden rows of positions n0 ..
+  const BwdPrep* prep;
+  const TokInfo* tinfo;
+  float* dX;                // d_hidden [N][H] (rows through tinfo)
   float* dW;                // d_shard rows v0..
+  int n0;                   // the unit's first position
   int ldg, nc_pad, vc_pad, vc, nc, H, acc_dx, acc_dw;
   int n_tiles, dw_first, first_slots;  // set by the launcher
 };

@@ -238,36 +238,106 @@ __global__ __launch_bounds__(256) void target_logit_kernel(const uint16_t* __res
   if (lane == 0) yt[row] = acc;
 }
 
-// Fixed-order tree sum over a 256-thread block (deterministic).
-__device__ __forceinline__ void block_sum2(double& a, long long& b) {
-  __shared__ double sa[256];
-  __shared__ long long sb[256];
-  sa[threadIdx.x] = a;
-  sb[threadIdx.x] = b;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if ((int)threadIdx.x < w) {
-      sa[threadIdx.x] += sa[threadIdx.x + w];
-      sb[threadIdx.x] += sb[threadIdx.x + w];
-    }
-    __syncthreads();
+// --------------------------------------------------------------------------
+// Backward preparation (one workgroup of 1024 threads): count the tokens whose
+// target is not ignore_index, decide whether leaving the others out saves a
+// 256-token tile (compact mode), and write the token info of every position
+// the backward runs over, kept tokens in ascending order. Thread t owns a run
+// of consecutive tokens; a block-wide prefix sum of the runs' counts gives
+// each thread its first position. The loss scale g = dloss / n_valid (mean)
+// or dloss (sum) is formed here, on the device, so dloss can come straight
+// from autograd; with reduction "none" each token carries its own dloss.
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void bwd_prep_kernel(const int* __restrict__ targets,
+                                                        const float* __restrict__ lse, int N, int ignore_index,
+                                                        const float* __restrict__ dloss, int reduction,
+                                                        int allow_compact, BwdPrep* __restrict__ prep,
+                                                        TokInfo* __restrict__ tinfo) {
+  __shared__ int wave_base[16];
+  __shared__ int s_total;
+  const int t = threadIdx.x;
+  const int lane = lane_id(), wave = t >> 6;
+  const int per = (((N + 1023) >> 10) + 3) & ~3;  // tokens per thread, a multiple of 4
+  const int r0 = min(t * per, N), r1 = min(r0 + per, N);
+  int cnt = 0;
+  int r = r0;
+  for (; r + 4 <= r1; r += 4) {
+    const int4 v = *reinterpret_cast<const int4*>(targets + r);  // r0 is a multiple of 4: aligned
+    cnt += (v.x != ignore_index) + (v.y != ignore_index) + (v.z != ignore_index) + (v.w != ignore_index);
   }
-  a = sa[0];
-  b = sb[0];
+  for (; r < r1; ++r) cnt += targets[r] != ignore_index;
+  int incl = cnt;  // inclusive prefix sum over the wave
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wave_base[wave] = incl;
+  __syncthreads();
+  if (t == 0) {
+    int acc = 0;
+    for (int w = 0; w < 16; ++w) {
+      const int v = wave_base[w];
+      wave_base[w] = acc;
+      acc += v;
+    }
+    s_total = acc;
+  }
+  __syncthreads();
+  const int n_valid = s_total;
+  const bool compact = allow_compact && ((n_valid + 255) & ~255) < ((N + 255) & ~255);
+  float gscale = 0.0f;
+  if (reduction == 0) gscale = (float)((double)dloss[0] / (double)n_valid);  // NaN / inf if n_valid = 0: unused then
+  if (reduction == 1) gscale = dloss[0];
+  int pos = compact ? wave_base[wave] + incl - cnt : r0;
+  for (r = r0; r < r1; ++r) {
+    const int tg = targets[r];
+    if (compact && tg == ignore_index) continue;
+    TokInfo ti;
+    ti.lse = lse[r];
+    ti.target = tg;
+    ti.g = reduction == 2 ? dloss[r] : gscale;
+    ti.row = r;
+    tinfo[pos++] = ti;
+  }
+  if (t == 0) {
+    BwdPrep p;
+    p.n_valid = n_valid;
+    p.n_eff = compact ? n_valid : N;
+    p.compact = compact ? 1 : 0;
+    p.gscale = gscale;
+    *prep = p;
+  }
 }
 
-// --------------------------------------------------------------------------
-// Backward scale: g = dloss / n_valid (mean) or dloss (sum), on the device so
-// dloss can come straight from autograd.
-// --------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void bwd_scale_kernel(const int* __restrict__ targets, int N, int ignore_index,
-                                                        const float* __restrict__ dloss, int reduction,
-                                                        float* __restrict__ gscale) {
-  double unused = 0.0;
-  long long c = 0;
-  for (int i = threadIdx.x; i < N; i += 256) c += (targets[i] != ignore_index) ? 1 : 0;
-  block_sum2(unused, c);
-  if (threadIdx.x == 0) gscale[0] = reduction == 0 ? (float)((double)dloss[0] / (double)c) : dloss[0];
+// Compact mode: copy the hidden rows of positions [n0, n0 + nc) (those that
+// exist) into xv, one block per row, 16-byte accesses.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __restrict__ X, uint16_t* __restrict__ xv,
+                                                          const BwdPrep* __restrict__ prep,
+                                                          const TokInfo* __restrict__ tinfo, int n0, int nc, int H) {
+  if (!prep->compact) return;
+  const int nv = min(nc, prep->n_eff - n0);
+  const int c8 = H >> 3;
+  for (int i = blockIdx.x; i < nv; i += gridDim.x) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(X + (size_t)tinfo[n0 + i].row * H);
+    u32x4* dst = reinterpret_cast<u32x4*>(xv + (size_t)i * H);
+    for (int c = threadIdx.x; c < c8; c += 256) dst[c] = src[c];
+  }
+}
+
+// Compact mode: zero the dX rows of ignored tokens, one block per row.
+__global__ __launch_bounds__(256) void zero_ignored_rows_kernel(float* __restrict__ dX,
+                                                                const BwdPrep* __restrict__ prep,
+                                                                const int* __restrict__ targets, int N, int H,
+                                                                int ignore_index) {
+  if (!prep->compact) return;
+  const int c4 = H >> 2;
+  const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int r = blockIdx.x; r < N; r += gridDim.x) {
+    if (targets[r] != ignore_index) continue;
+    f32x4* d = reinterpret_cast<f32x4*>(dX + (size_t)r * H);
+    for (int c = threadIdx.x; c < c4; c += 256) d[c] = z;
+  }
 }
 
 // --------------------------------------------------------------------------
@@ -331,27 +401,28 @@ __device__ __forceinline__ void recompute_g_tile(const BwdGArgs& a, int id, LCE_
   const int wm = wave / kWN, wn = wave % kWN;
   int tt, tv;
   xcd_tile(id, a.n_tt, a.n_tv, tt, tv);
+  // positions of this unit that exist (the host plans for every token; the
+  // backward runs over n_eff of them)
+  const int nv = min(a.nc, a.prep->n_eff - a.n0);
+  if (tt * kBN >= nv) return;
+  // the hidden rows of the unit's positions: gathered (compact mode) or X's own
+  const uint16_t* xs = a.prep->compact ? a.xv : a.X + (size_t)a.n0 * a.H;
 
   // per-lane token info, loaded before the main loop (unconditionally, from a
-  // clamped row, so that the loads complete under the loop's first wait) and
-  // turned into (log2-domain lse, gradient scale, target row in this tile)
-  // after it
-  float lse_raw[kNI], gs_raw[kNI];
-  int t_raw[kNI];
+  // clamped position, so that the loads complete under the loop's first wait)
+  // and turned into (log2-domain lse, gradient scale, target row in this
+  // tile) after it
+  TokInfo ti[kNI];
   bool valid[kNI];
 #pragma unroll
   for (int j = 0; j < kNI; ++j) {
     const int rr = tt * kBN + wn * kWaveN + kBlk * j + (lane & 15);
-    const int row = a.n0 + rr;
-    valid[j] = rr < a.nc && row < a.N;
-    const int rc = valid[j] ? row : a.n0;  // a.n0 < a.N: the tile exists
-    lse_raw[j] = a.lse[rc];
-    t_raw[j] = a.targets[rc];
-    gs_raw[j] = a.gscale[a.g_per_token ? rc : 0];
+    valid[j] = rr < nv;
+    ti[j] = a.tinfo[a.n0 + (valid[j] ? rr : tt * kBN)];
   }
   KContigLoader lw, lx;
   lw.init(a.Ws, a.H, a.v0 + tv * kBM, a.Vs, wave, lane);
-  lx.init(a.X, a.H, a.n0 + tt * kBN, a.N, wave, lane);
+  lx.init(xs, a.H, tt * kBN, nv, wave, lane);
   Acc acc;
   tile_mainloop<false, false>(lw, lx, a.H, lds, acc);
 
@@ -363,13 +434,13 @@ __device__ __forceinline__ void recompute_g_tile(const BwdGArgs& a, int id, LCE_
     g[j] = 0.0f;
     tcol[j] = -1;
     if (valid[j]) {
-      lse2[j] = lse_raw[j] * kLog2e;
-      const int t = t_raw[j];
+      lse2[j] = ti[j].lse * kLog2e;
+      const int t = ti[j].target;
       if (t != a.ignore_index) {
         if (t < 0 || t >= a.V) {
           g[j] = __builtin_nanf("");
         } else {
-          g[j] = gs_raw[j];
+          g[j] = ti[j].g;
           tcol[j] = t - (a.vocab_base + tv * kBM);
         }
       }
@@ -408,32 +479,43 @@ __device__ __forceinline__ void recompute_g_tile(const BwdGArgs& a, int id, LCE_
 }
 
 // Stores (accumulate = 0) or adds (accumulate = 1) the fp32 tile into
-// C[m0 + r][n0 + c] for r < m_valid - m0, c < n_valid - n0 (n_valid a multiple
-// of 4). The tile goes through LDS in two halves of 128 rows (the rows of the
-// waves with wm = 0, then wm = 1), so that global memory sees 16-byte accesses
-// along whole rows. For each half, a thread issues all of its loads of C
-// before the half is staged, so they fly while the accumulators are written
-// to LDS and the half costs one round trip to memory. LDS row r holds the 256
-// floats of the row, with column c stored at c ^ (16 ((r >> 2) & 3)), so the
-// four 16-lane groups of an accumulator write (rows r, r + 4, r + 8, r + 12,
-// 16 columns each) use different banks. Needs the 128 KB of LDS free (the
-// main loop ends on a barrier).
+// C[row(m0 + r)][n0 + c] for r < m_valid - m0, c < n_valid - n0 (n_valid a
+// multiple of 4), where row(i) = rmap[i].row when a row map is given (the dX
+// rows of the positions) and i otherwise. The tile goes through LDS in two
+// halves of 128 rows (the rows of the waves with wm = 0, then wm = 1), so that
+// global memory sees 16-byte accesses along whole rows. For each half, a
+// thread issues all of its loads of C before the half is staged, so they fly
+// while the accumulators are written to LDS and the half costs one round trip
+// to memory. LDS row r holds the 256 floats of the row, with column c stored
+// at c ^ (16 ((r >> 2) & 3)), so the four 16-lane groups of an accumulator
+// write (rows r, r + 4, r + 8, r + 12, 16 columns each) use different banks.
+// Needs the 128 KB of LDS free (the main loop ends on a barrier).
 // Thread t handles 16-byte chunk (t & 63) of rows (t >> 6) + 8 k, k < kIt.
 template <int kIt, bool kFull>
+__device__ __forceinline__ void half_rows(const TokInfo* __restrict__ rmap, int r0, int m_valid, int (&rows)[kIt]) {
+#pragma unroll
+  for (int k = 0; k < kIt; ++k) {
+    const int gr = r0 + k * (kThreads / 64) + (threadIdx.x >> 6);
+    rows[k] = gr;
+    if (rmap && (kFull || gr < m_valid)) rows[k] = rmap[gr].row;
+  }
+}
+template <int kIt, bool kFull>
 __device__ __forceinline__ void load_half(const float* __restrict__ C, int ldc, int r0, int m_valid, int n0,
-                                          int n_valid, float4 (&old)[kIt]) {
+                                          int n_valid, const int (&rows)[kIt], float4 (&old)[kIt]) {
   const int c = threadIdx.x & 63;
   const int gc = n0 + 4 * c;
 #pragma unroll
   for (int k = 0; k < kIt; ++k) {
     const int gr = r0 + k * (kThreads / 64) + (threadIdx.x >> 6);
     old[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    if (kFull || (gr < m_valid && gc < n_valid)) old[k] = *reinterpret_cast<const float4*>(C + (size_t)gr * ldc + gc);
+    if (kFull || (gr < m_valid && gc < n_valid))
+      old[k] = *reinterpret_cast<const float4*>(C + (size_t)rows[k] * ldc + gc);
   }
 }
 template <int kIt, bool kFull, bool kAcc>
 __device__ __forceinline__ void store_half(float* __restrict__ C, int ldc, int r0, int m_valid, int n0, int n_valid,
-                                           const float* tile, const float4 (&old)[kIt]) {
+                                           const int (&rows)[kIt], const float* tile, const float4 (&old)[kIt]) {
   const int c = threadIdx.x & 63;
   const int gc = n0 + 4 * c;
 #pragma unroll
@@ -450,14 +532,15 @@ __device__ __forceinline__ void store_half(float* __restrict__ C, int ldc, int r
       }
       // non-temporal: the next add to this tile comes from a later launch
       const f32x4 nv = {v.x, v.y, v.z, v.w};
-      __builtin_nontemporal_store(nv, reinterpret_cast<f32x4*>(C + (size_t)gr * ldc + gc));
+      __builtin_nontemporal_store(nv, reinterpret_cast<f32x4*>(C + (size_t)rows[k] * ldc + gc));
     }
   }
 }
 
 template <bool kFull, bool kAcc>
-__device__ __forceinline__ void store_tile_impl(const Acc& acc, float* __restrict__ C, int ldc, int m0, int m_valid,
-                                                int n0, int n_valid, char* ldsg) {
+__device__ __forceinline__ void store_tile_impl(const Acc& acc, float* __restrict__ C, int ldc,
+                                                const TokInfo* __restrict__ rmap, int m0, int m_valid, int n0,
+                                                int n_valid, char* ldsg) {
   const int wave = wave_id();
   const int lane = lane_id();
   const int wm = wave / kWN, wn = wave % kWN;
@@ -466,8 +549,10 @@ __device__ __forceinline__ void store_tile_impl(const Acc& acc, float* __restric
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int r0 = m0 + 128 * h;
+    int rows[kIt];
+    half_rows<kIt, kFull>(rmap, r0, m_valid, rows);
     float4 old[kIt];
-    if (kAcc) load_half<kIt, kFull>(C, ldc, r0, m_valid, n0, n_valid, old);
+    if (kAcc) load_half<kIt, kFull>(C, ldc, r0, m_valid, n0, n_valid, rows, old);
     if (wm == h) {
 #pragma unroll
       for (int i = 0; i < kMI; ++i)
@@ -482,24 +567,32 @@ __device__ __forceinline__ void store_tile_impl(const Acc& acc, float* __restric
         }
     }
     __syncthreads();
-    store_half<kIt, kFull, kAcc>(C, ldc, r0, m_valid, n0, n_valid, tile, old);
+    store_half<kIt, kFull, kAcc>(C, ldc, r0, m_valid, n0, n_valid, rows, tile, old);
     __syncthreads();
   }
 }
 
-__device__ __forceinline__ void store_tile(const Acc& acc, float* __restrict__ C, int ldc, int m0, int m_valid,
-                                           int n0, int n_valid, int accumulate, char* ldsg) {
+__device__ __forceinline__ void store_tile(const Acc& acc, float* __restrict__ C, int ldc,
+                                           const TokInfo* __restrict__ rmap, int m0, int m_valid, int n0,
+                                           int n_valid, int accumulate, char* ldsg) {
   const bool full = m0 + kBM <= m_valid && n0 + kBN <= n_valid;
   if (full && accumulate)
-    store_tile_impl<true, true>(acc, C, ldc, m0, m_valid, n0, n_valid, ldsg);
+    store_tile_impl<true, true>(acc, C, ldc, rmap, m0, m_valid, n0, n_valid, ldsg);
   else if (full)
-    store_tile_impl<true, false>(acc, C, ldc, m0, m_valid, n0, n_valid, ldsg);
+    store_tile_impl<true, false>(acc, C, ldc, rmap, m0, m_valid, n0, n_valid, ldsg);
   else if (accumulate)
-    store_tile_impl<false, true>(acc, C, ldc, m0, m_valid, n0, n_valid, ldsg);
+    store_tile_impl<false, true>(acc, C, ldc, rmap, m0, m_valid, n0, n_valid, ldsg);
   else
-    store_tile_impl<false, false>(acc, C, ldc, m0, m_valid, n0, n_valid, ldsg);
+    store_tile_impl<false, false>(acc, C, ldc, rmap, m0, m_valid, n0, n_valid, ldsg);
 }
 
+// The K loop of a gradient tile runs over the live part of its contraction
+// only: the vocabulary chunk rounded up to the 64 of a stage for dX (the G
+// columns past the chunk are zero), and for dW the positions of the unit that
+// exist, rounded up likewise (G rows past them are zero; their X rows are
+// clamped to the last existing one). A dW tile with nothing to contract
+// writes zeros (or, accumulating, leaves its rows as they are); a dX tile
+// past the existing positions has no rows to write.
 __device__ __forceinline__ void grad_tile(const GradArgs& a, int id, LCE_LDS char* lds, char* ldsg) {
   const int wave = wave_id();
   const int lane = lane_id();
@@ -515,20 +608,32 @@ __device__ __forceinline__ void grad_tile(const GradArgs& a, int id, LCE_LDS cha
   if (id >= rows * a.n_tiles) return;  // padding slot
   int tm, tn;
   xcd_tile(id, rows, a.n_tiles, tm, tn);
+  const int nv = min(a.nc, a.prep->n_eff - a.n0);
   Acc acc;
   if (is_dx) {
+    if (tm * kBM >= nv) return;
     KContigLoader la;
     KMajorLoader lb;
-    la.init(a.G, a.ldg, tm * kBM, a.nc_pad, wave, lane);
+    la.init(a.G, a.ldg, tm * kBM, nv, wave, lane);
     lb.init(a.Wc, a.H, tn * kBN, a.H, a.vc, wave, lane);
-    tile_mainloop<false, true>(la, lb, a.vc_pad, lds, acc);
-    store_tile(acc, a.dX, a.H, tm * kBM, a.nc, tn * kBN, a.H, a.acc_dx, ldsg);
+    tile_mainloop<false, true>(la, lb, (a.vc + kBK - 1) / kBK * kBK, lds, acc);
+    store_tile(acc, a.dX, a.H, a.tinfo + a.n0, tm * kBM, nv, tn * kBN, a.H, a.acc_dx, ldsg);
   } else {
-    KMajorLoader la, lb;
-    la.init(a.G, a.ldg, tm * kBM, a.vc_pad, a.nc_pad, wave, lane);
-    lb.init(a.Xc, a.H, tn * kBN, a.H, a.nc, wave, lane);
-    tile_mainloop<true, true>(la, lb, a.nc_pad, lds, acc);
-    store_tile(acc, a.dW, a.H, tm * kBM, a.vc, tn * kBN, a.H, a.acc_dw, ldsg);
+    if (nv <= 0) {
+      if (a.acc_dw) return;
+#pragma unroll
+      for (int i = 0; i < kMI; ++i)
+#pragma unroll
+        for (int j = 0; j < kNI; ++j) acc[i][j] = f32x4{};
+    } else {
+      const int k_live = (nv + kBK - 1) / kBK * kBK;
+      const uint16_t* xs = a.prep->compact ? a.xv : a.X + (size_t)a.n0 * a.H;
+      KMajorLoader la, lb;
+      la.init(a.G, a.ldg, tm * kBM, a.vc_pad, k_live, wave, lane);
+      lb.init(xs, a.H, tn * kBN, a.H, nv, wave, lane);
+      tile_mainloop<true, true>(la, lb, k_live, lds, acc);
+    }
+    store_tile(acc, a.dW, a.H, nullptr, tm * kBM, a.vc, tn * kBN, a.H, a.acc_dw, ldsg);
   }
 }
 
@@ -666,9 +771,24 @@ hipError_t launch_target_logit(const uint16_t* X, int N, int H, const ShardTable
   return last();
 }
 
-hipError_t launch_bwd_scale(const int* targets, int N, int ignore_index, const float* dloss, int reduction,
-                            float* gscale, hipStream_t st) {
-  hipLaunchKernelGGL(bwd_scale_kernel, dim3(1), dim3(256), 0, st, targets, N, ignore_index, dloss, reduction, gscale);
+hipError_t launch_bwd_prep(const int* targets, const float* lse, int N, int ignore_index, const float* dloss,
+                           int reduction, int allow_compact, BwdPrep* prep, TokInfo* tinfo, hipStream_t st) {
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3(1), dim3(1024), 0, st, targets, lse, N, ignore_index, dloss, reduction,
+                     allow_compact, prep, tinfo);
+  return last();
+}
+
+hipError_t launch_gather_rows(const uint16_t* X, uint16_t* xv, const BwdPrep* prep, const TokInfo* tinfo, int n0,
+                              int nc, int H, hipStream_t st) {
+  const int blocks = nc < 2048 ? (nc < 1 ? 1 : nc) : 2048;  // grid-stride over rows beyond that
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(blocks), dim3(256), 0, st, X, xv, prep, tinfo, n0, nc, H);
+  return last();
+}
+
+hipError_t launch_zero_ignored_rows(float* dX, const BwdPrep* prep, const int* targets, int N, int H,
+                                    int ignore_index, hipStream_t st) {
+  const int blocks = N < 2048 ? (N < 1 ? 1 : N) : 2048;
+  hipLaunchKernelGGL(zero_ignored_rows_kernel, dim3(blocks), dim3(256), 0, st, dX, prep, targets, N, H, ignore_index);
   return last();
 }
 

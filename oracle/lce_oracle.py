@@ -211,3 +211,24 @@ def token_rows(x_rows, w, t_rows, g_rows, ignore_index: int = IGNORE_INDEX):
     p[rows, t[rows]] -= 1.0
     p *= np.where(valid, g, 0.0)[:, None]
     return lse, tok, p @ w
+
+
+def weight_rows(x, w_rows, v_ids, targets, lse, g, ignore_index: int = IGNORE_INDEX):
+    """Selected rows of dW, given every token's normalizer lse and loss scale g.
+
+    The gradient of vocabulary row v is a sum over tokens:
+        dW_v = sum_i g_i (exp(x_i . w_v - lse_i) - [t_i = v]) x_i,
+    which needs only that row of W, all of X and the per-token lse and g (g_i
+    = dloss / n_valid for valid tokens, 0 for ignored ones), so a few rows of a
+    large problem can be checked one by one at N x H cost each. x: [N][H],
+    w_rows: [k][H] (the rows v_ids of W), lse, g: [N]. Returns [k][H].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w_rows = np.asarray(w_rows, dtype=np.float64)
+    t = np.asarray(targets, dtype=np.int64)
+    lse = np.asarray(lse, dtype=np.float64)
+    g = np.where(t != ignore_index, np.asarray(g, dtype=np.float64), 0.0)
+    ids = np.asarray(v_ids, dtype=np.int64)
+    z = x @ w_rows.T                                         # the rows' logits, every token: [N][k]
+    coef = g[:, None] * (np.exp(z - lse[:, None]) - (t[:, None] == ids[None, :]))   # dloss/dlogit
+    return coef.T @ x

@@ -283,6 +283,25 @@ def check_row_samples(orc, seed=6):
     np.testing.assert_allclose(dx, base.d_hidden[rows], rtol=1e-12, atol=1e-15)
 
 
+def check_weight_rows(orc, seed=10):
+    """Selected dW rows given lse and g equal the rows of the full definition's
+    dW (and of torch's autograd), ignored tokens and a row with several
+    targets included."""
+    import torch
+    rng = np.random.default_rng(seed)
+    x, w, t = rand_instance(rng, 14, 5, 9, ignore=3)
+    t[[0, 4]] = 2                                   # two tokens share target 2
+    base = orc.cross_entropy(x, w, t)
+    g = np.where(t != -100, 1.0 / base.n_valid, 0.0)
+    ids = [0, 2, 8]
+    got = orc.weight_rows(x, w[ids], ids, t, base.lse, g)
+    np.testing.assert_allclose(got, base.d_weight[ids], rtol=1e-12, atol=1e-15)
+    wt = torch.tensor(w, requires_grad=True)
+    loss = torch.nn.functional.cross_entropy(torch.tensor(x) @ wt.T, torch.tensor(t), ignore_index=-100)
+    loss.backward()
+    np.testing.assert_allclose(got, wt.grad.numpy()[ids], rtol=1e-10, atol=1e-15)
+
+
 def all_small_checks(orc):
     """Every pin that runs in about a second (used by the planted-mistake test)."""
     check_bf16_widening(orc)
@@ -296,3 +315,4 @@ def all_small_checks(orc):
     check_logistic(orc)
     check_invariants(orc)
     check_row_samples(orc)
+    check_weight_rows(orc)

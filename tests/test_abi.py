@@ -72,7 +72,7 @@ def _bwd(d, hidden=FAKE, lse=FAKE, dloss=FAKE, dx=FAKE, dws=None, ws=FAKE, ws_by
     (_dims(p=0), lce.ERR_INVALID_ARG),
     (_dims(p=257, v=257 * 4), lce.ERR_INVALID_ARG),
     (_dims(v=1000, p=3), lce.ERR_INVALID_ARG),
-    (_dims(flags=8), lce.ERR_INVALID_ARG),
+    (_dims(flags=16), lce.ERR_INVALID_ARG),
     (_dims(red=3), lce.ERR_INVALID_ARG),
     (_dims(h=100), lce.ERR_UNSUPPORTED),
     (_dims(n=1 << 22, h=1024), lce.ERR_UNSUPPORTED),
@@ -116,7 +116,8 @@ def test_workspace_too_small():
     d = _dims()
     need = lce.lib().lce_workspace_bytes(ctypes.byref(d))
     assert need > 0
-    assert _fwd(d, ws_bytes=need - 1) == lce.ERR_WORKSPACE
+    assert _fwd(d, ws_bytes=lce.state_bytes(d) - 1) == lce.ERR_WORKSPACE
+    assert "forward needs %d" % lce.state_bytes(d) in lce.lib().lce_last_error().decode()
     assert _bwd(d, ws_bytes=need - 1) == lce.ERR_WORKSPACE
     assert "needs %d" % need in lce.lib().lce_last_error().decode()
 
@@ -129,14 +130,14 @@ def test_status_strings():
 
 
 def test_workspace_is_bounded_independently_of_vocab():
-    # N and H fixed, V swept: the workspace never holds a logit strip (N x V/P)
+    # N and H fixed, V swept: the workspace never holds a logit strip (N x V/P).
+    # It is O(N) per-token state, the kept tokens' hidden rows (N x H bf16) and
+    # two G chunks of at most 2^27 bf16 elements each, whatever V is.
     n, h, p = 16384, 4096, 8
-    sizes = [lce.workspace_bytes(n, h, p * vs, p) for vs in (2004, 4008, 8016, 16032, 32064, 64128)]
-    bound = lce.workspace_bytes(n, h, p * 8192, p)   # the largest vocabulary chunk
-    assert max(sizes) <= bound
-    strip_bytes = n * 16032 * 4
-    assert bound < strip_bytes
-    # and it is O(N): doubling V at fixed N never grows it past the bound
+    bound = 64 * n + n * h * 2 + 2 * (2 ** 27) * 2 + 4096
+    for vs in (2004, 4008, 8016, 16032, 32064, 64128, 256512):
+        assert lce.workspace_bytes(n, h, p * vs, p) <= bound, vs
+    assert bound < n * 16032 * 4          # far below one logit strip at the large workload
     assert lce.workspace_bytes(n, h, 8 * 128256 * 2, 8) <= bound
 
 
@@ -194,12 +195,15 @@ def test_per_token_reduction_needs_token_loss():
 
 
 def test_bf16_gradient_workspace():
-    # fp32 accumulators for d_hidden (N x H) and one gradient chunk (<= 8192 x H)
+    # fp32 accumulators for d_hidden (N x H) and one gradient chunk (at most 16384 x H)
     n, h, v, p = 1000, 512, 8 * 20000, 8
     plain = lce.workspace_bytes(n, h, v, p)
     bf16 = lce.workspace_bytes(n, h, v, p, flags=lce.FLAG_BF16_GRADS)
-    assert n * h * 4 + 256 * h * 4 <= bf16 - plain <= n * h * 4 + 8192 * h * 4 + 1024
+    assert n * h * 4 + 256 * h * 4 <= bf16 - plain <= n * h * 4 + 16384 * h * 4 + 1024
     assert lce.workspace_bytes(n, h, v, p, flags=lce.FLAG_ACCUMULATE_DX | lce.FLAG_ACCUMULATE_DW) == plain
+    # the accumulator does not grow with V past the chunk bound
+    assert lce.workspace_bytes(n, h, 8 * 200000, 8, flags=lce.FLAG_BF16_GRADS) - \
+        lce.workspace_bytes(n, h, 8 * 200000, 8) <= n * h * 4 + 16384 * h * 4 + 1024
 
 
 def test_ring_payload_choice():

@@ -28,8 +28,14 @@ SHAPES = [
     ("one vocab row per shard", 3, 64, 4, 4, 0.0, 1.0),
     ("V=1", 5, 64, 1, 1, 0.0, 1.0),
     ("256 shards", 300, 64, 256 * 3, 256, 0.1, 0.3),
-    ("two token chunks", 16384 + 300, 64, 520, 2, 0.05, 0.3),
-    ("two vocab chunks", 300, 64, 2 * 9000, 2, 0.05, 0.3),
+    # backward chunking (G chunks of at most 2^27 elements, vocabulary chunks of
+    # at most 16384 rows): two token chunks and two vocabulary chunks per shard
+    ("two token and two vocab chunks", 24000, 64, 2 * 20000, 2, 0.05, 0.3),
+    ("two vocab chunks", 300, 64, 2 * 20000, 2, 0.05, 0.3),
+    # ignored tokens left out of the backward (a token tile saved): ragged,
+    # and with the second token chunk left empty
+    ("ignored tokens left out", 1000, 128, 3000, 3, 0.3, 0.1),
+    ("half ignored, empty second token chunk", 24000, 64, 2 * 20000, 2, 0.5, 0.3),
     ("large logits", 333, 512, 2048, 2, 0.1, 0.5),
 ]
 

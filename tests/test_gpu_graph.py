@@ -30,8 +30,8 @@ def _run(lce, hidden, shards, targets, ws, dx, dws, dloss):
     return loss, lse
 
 
-@pytest.mark.parametrize("dims", [(700, 256, 4 * 1000, 4), (16384 + 300, 64, 520, 2)],
-                         ids=["one chunk", "two token chunks"])
+@pytest.mark.parametrize("dims", [(700, 256, 4 * 1000, 4), (24000, 64, 2 * 20000, 2)],
+                         ids=["one chunk", "two token and two vocab chunks"])
 def test_graph_replays_match_eager(dims):
     import torch
     import memory_bounded_vocabulary_amd as lce

@@ -22,6 +22,19 @@ def test_workload_parity(name):
     compare(gpu, oracle_for(b), name)
 
 
+def test_large_width_two_token_chunks():
+    """The large workload's H, V and P with N = 16384 + 300 tokens: the backward
+    runs two token chunks and two vocabulary chunks per shard (the fp32 dW of a
+    shard accumulates over the token chunks), compared element by element with
+    the oracle (about 5e13 float64 flops on the host)."""
+    w = workloads.WORKLOADS["large"].with_tokens(16384 + 300)
+    say("workload slice", w.name, "two token chunks at H =", w.hidden)
+    b = workloads.make(w)
+    gpu = run_lce(*to_device(b))
+    say("oracle on the host ...")
+    compare(gpu, oracle_for(b), w.name)
+
+
 @pytest.mark.parametrize("name", ["large", "long", "stress"])
 def test_workload_slice_parity(name):
     w = workloads.WORKLOADS[name].with_tokens(777)

@@ -13,7 +13,12 @@ so:
   up to the rounding of G to bf16 (unit roundoff 2^-8 per element, random
   sign: about 2^-8/sqrt(3) times the root-sum-square of the column; the bound
   used is 2^-5 times it);
-* the mean loss must equal the mean of the per-token losses.
+* the mean loss must equal the mean of the per-token losses;
+* a dozen vocabulary rows of dW (shard edges, the most frequent target, the
+  last id, random ones) are computed one by one in float64 from the row's
+  definition, given every token's lse and loss scale (oracle.weight_rows, at
+  N x H cost per row); lse is the GPU's, itself checked on the sampled rows
+  above, and an lse error e moves a row by a relative e at most.
 """
 import numpy as np
 import pytest
@@ -82,6 +87,20 @@ def test_full_size_sampled(name):
     say(f"{name}: max_h |sum_v dW_vh|/rss_h={e_col:.2e} <dX,X>={lhs:.6e} <dW,W>={rhs:.6e} rel={e_ip:.2e}")
     assert e_col <= 2.0 ** -5
     assert e_ip <= 1e-3
+
+    # sampled dW rows against their float64 definition
+    vs = w.shard_rows
+    rng = np.random.default_rng(1)
+    ids = sorted({0, vs - 1, vs, w.vocab - vs, w.vocab - 1, int(np.bincount(b.targets[b.targets >= 0]).argmax())} |
+                 {int(i) for i in rng.choice(w.vocab, size=6, replace=False)})
+    lse_all = lse.double().cpu().numpy()
+    x64 = oracle.bf16_to_f64(b.hidden)
+    ref_dw = oracle.weight_rows(x64, oracle.bf16_to_f64(b.weight[ids]), ids, b.targets, lse_all, g)
+    del x64
+    got_dw = np.stack([dws[i // vs][i % vs].double().cpu().numpy() for i in ids])
+    e_dw = float(np.max(np.abs(got_dw - ref_dw)) / np.max(np.abs(ref_dw)))
+    say(f"{name}: dW rows {ids}: rel={e_dw:.2e}")
+    assert e_dw <= GRAD_TOL
     assert all(bool(torch.isfinite(d).all().item()) for d in dws) and bool(torch.isfinite(dx).all().item())
 
 

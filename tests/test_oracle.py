@@ -65,6 +65,10 @@ def test_row_samples():
     pins.check_row_samples(oracle)
 
 
+def test_weight_rows():
+    pins.check_weight_rows(oracle)
+
+
 def test_large_logits_stay_finite():
     # logits of order 1e3 overflow a naive exp; the max-shifted form must not
     rng = np.random.default_rng(9)
@@ -117,6 +121,8 @@ MUTANTS = {
     "row sample one-hot dropped": ("p[rows, t[rows]] -= 1.0\n    p *= np.where", "p *= np.where"),
     "per-token scale ignores the token": ("scale = np.asarray(dloss, dtype=np.float64)",
                                           "scale = np.full(t.shape, np.mean(dloss))"),
+    "weight row one-hot at the wrong id": ("(t[:, None] == ids[None, :])", "(t[:, None] == ids[None, :] + 1)"),
+    "weight row without the normalizer": ("np.exp(z - lse[:, None])", "np.exp(z)"),
     "per-token loss reported as a mean": ('if reduction in ("sum", "none"):', 'if reduction == "sum":'),
 }
 
