@@ -424,7 +424,10 @@ __device__ __forceinline__ void recompute_g_tile(const BwdGArgs& a, int id, LCE_
   lw.init(a.Ws, a.H, a.v0 + tv * kBM, a.Vs, wave, lane);
   lx.init(xs, a.H, tt * kBN, nv, wave, lane);
   Acc acc;
-  tile_mainloop<false, false>(lw, lx, a.H, lds, acc);
+  // load addresses formed at each issue (as in the forward): with the two
+  // K-contiguous operands this loop runs about 10 % faster than with the
+  // addresses hoisted out of it
+  tile_mainloop<false, false, false, true>(lw, lx, a.H, lds, acc);
 
   float lse2[kNI], g[kNI];
   int tcol[kNI];
