@@ -3,18 +3,24 @@
 //
 // Schedule (one rank's share of "Flattening Every Memory Peak in Long-Context
 // Mixture-of-Experts Training", section 3.2, Ring-DTP):
-//   forward   target logits; round k = 0..P-1 folds shard order[k] into the
-//             per-token running (m, z); then a finalize launch merges the
-//             split states into lse = m + log z and the token losses, and a
+//   forward   round k = 0..P-1 folds shard order[k] into the per-token
+//             running (m, z), and the tile holding a token's target writes
+//             its target logit; then a finalize launch merges the split
+//             states into lse = m + log z and the token losses, and a
 //             one-block launch sums the loss.
-//   backward  g = dloss / n_valid; then for every unit (shard in ring order,
-//             vocabulary chunk, token chunk): recompute the logit block from
-//             lse and form G in bf16, then dX += G W_chunk and dW_chunk +=
-//             G^T X_chunk (fp32). One launch runs the GEMMs of unit j - 1 with
-//             the recompute of unit j (two G buffers alternate). The GEMMs
-//             read W, X and G as they lie in memory; nothing is transposed.
-// Transient device memory is O(N) plus fixed-size chunks: no logit strip
-// (N x V/P) is ever formed.
+//   backward  a preparation launch forms the loss scale and the list of
+//             positions the backward runs over (only the tokens whose target
+//             is not ignore_index, when leaving the others out saves a token
+//             tile; their hidden rows are gathered per token chunk); then for
+//             every unit (token chunk, shard in ring order, vocabulary chunk):
+//             recompute the logit block from lse and form G in bf16, then
+//             dX += G W_chunk and dW_chunk += G^T X_chunk (fp32). One launch
+//             runs the GEMMs of unit j - 1 with the recompute of unit j (two
+//             G buffers alternate). The GEMMs read W, X and G as they lie in
+//             memory; nothing is transposed.
+// Transient device memory is O(N) per-token state, the gathered hidden rows
+// (at most N x H bf16) and fixed-size G chunks: no logit strip (N x V/P) is
+// ever formed.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -230,7 +236,7 @@ int hip_status(hipError_t e, const char* what) {
 
 // ---- optional per-launch event trace (see lce_trace_enable) ----
 enum Kind { kTargetLogit, kFwdRound, kFinalize, kBwdPrep, kGather, kBwdG, kBwdStep, kGradGemm, kConvert, kKinds };
-const char* const kKindName[kKinds] = {"target_logit", "fwd_round", "finalize", "bwd_prep",     "gather",
+const char* const kKindName[kKinds] = {"target_init", "fwd_round", "finalize", "bwd_prep",     "gather",
                                        "bwd_g",        "bwd_step",  "grad_gemm", "bf16_convert"};
 
 // Algorithmic work of one launch: a fixed part plus, for backward launches,
@@ -303,16 +309,10 @@ lce::FwdArgs fwd_args(const Plan& p, const lce_dims* d, const void* hidden, cons
   return a;
 }
 
-int run_target_logit(const Plan& p, const lce::FwdArgs& a, const lce::ShardTable& by_id, int s_lo, int s_hi, int init,
-                     hipStream_t s) {
-  const double dN = double(p.N), dH = double(p.H);
-  return hip_status(traced(kTargetLogit, Work(0.0, 4.0 * dN * dH + 8.0 * dN), s,
-                           [&] {
-                             return lce::launch_target_logit(a.X, a.N, a.H, by_id, a.Vs, int(p.V), s_lo, s_hi,
-                                                             a.targets, a.ignore_index, const_cast<float*>(a.yt), init,
-                                                             s);
-                           }),
-                    "target logits");
+int run_init_target_logits(const Plan& p, const lce::FwdArgs& a, hipStream_t s) {
+  return hip_status(traced(kTargetLogit, Work(0.0, 8.0 * double(p.N)), s,
+                           [&] { return lce::launch_init_target_logits(a.targets, a.N, a.ignore_index, a.yt, s); }),
+                    "target logit init");
 }
 
 int run_fwd_rounds(const Plan& p, const lce::FwdArgs& a, const lce::ShardTable& by_round, int k0, int k1, int first,
@@ -647,13 +647,13 @@ int run_forward(const Plan& p, const lce_dims* d, const void* hidden, const void
                 const int32_t* order, const int32_t* targets, float* loss, float* lse, float* token_loss, char* ws,
                 hipStream_t s) {
   if (d->n_tokens == 0) return run_empty_loss(d, loss, s);
-  lce::ShardTable by_id{}, by_round{};
+  lce::ShardTable by_round{};
   for (int k = 0; k < d->n_shards; ++k) {
-    by_id.p[k] = static_cast<const uint16_t*>(w_shards[k]);
     by_round.p[k] = static_cast<const uint16_t*>(w_shards[order[k]]);
+    by_round.id[k] = order[k];
   }
   const lce::FwdArgs a = fwd_args(p, d, hidden, targets, ws, loss, lse, token_loss);
-  int st = run_target_logit(p, a, by_id, 0, d->n_shards, 1, s);
+  int st = run_init_target_logits(p, a, s);
   if (st) return st;
   // All rounds in one launch when every workgroup is resident at once (its
   // state then stays in registers); else one launch per round.
@@ -799,13 +799,15 @@ int lce_fwd_round(const lce_dims* d, int round, int shard_index, const void* hid
   g_last_error.clear();
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  lce::ShardTable by_id{}, by_round{};
-  by_id.p[shard_index] = static_cast<const uint16_t*>(w_shard);
+  lce::ShardTable by_round{};
   by_round.p[0] = static_cast<const uint16_t*>(w_shard);
+  by_round.id[0] = shard_index;
   const lce::FwdArgs a = fwd_args(p, d, hidden, targets, ws, nullptr, nullptr, nullptr);
   if (d->n_tokens == 0) return LCE_OK;  // nothing to fold
-  st = run_target_logit(p, a, by_id, shard_index, shard_index + 1, round == 0, s);
-  if (st) return st;
+  if (round == 0) {
+    st = run_init_target_logits(p, a, s);
+    if (st) return st;
+  }
   return run_fwd_rounds(p, a, by_round, 0, 1, round == 0, s);
 }
 

@@ -8,10 +8,11 @@ namespace lce {
 
 constexpr int kMaxShards = 256;
 
-// Device pointers of all vocabulary shards, passed by value as a kernel
-// argument (2 KB) so no host->device copy is needed.
+// Device pointers of the vocabulary shards (and their ids), passed by value
+// as a kernel argument (3 KB) so no host->device copy is needed.
 struct ShardTable {
   const uint16_t* p[kMaxShards];
+  int id[kMaxShards];
 };
 
 // Forward rounds [k_begin, k_end) in one launch (shards.p[k] is the shard met in
@@ -19,7 +20,7 @@ struct ShardTable {
 struct FwdArgs {
   const uint16_t* X;        // hidden [N][H]
   const int* targets;
-  const float* yt;          // target logits from launch_target_logit
+  float* yt;                // target logits, written by the tile that holds each
   float2* state;            // [S][state_ld] per-split (m, z), log2 domain
   double2* partials;        // [token_blocks] (loss sum, count)
   float* lse;               // [N]
@@ -31,10 +32,10 @@ hipError_t launch_fwd_rounds(const FwdArgs& a, const ShardTable& shards, int k_b
                              hipStream_t st);
 // After the last round: lse, token losses, block partials, then the loss (two launches).
 hipError_t launch_finalize(const FwdArgs& a, hipStream_t st);
-// Target logits of the tokens whose target lies in shards [s_lo, s_hi)
-// (shards.p indexed by shard id); `init` first resets yt.
-hipError_t launch_target_logit(const uint16_t* X, int N, int H, const ShardTable& shards, int Vs, int V, int s_lo,
-                               int s_hi, const int* targets, int ignore_index, float* yt, int init, hipStream_t st);
+// Before the first round: yt = 0 for ignored tokens, NaN for the others (the
+// rounds fill in each target logit when its tile is folded; a target outside
+// [0, V) is never filled, so its token's loss, and the mean, stay NaN).
+hipError_t launch_init_target_logits(const int* targets, int N, int ignore_index, float* yt, hipStream_t st);
 // Backward preparation, written on the device by launch_bwd_prep. Only
 // tokens whose target is not ignore_index can have a nonzero gradient row.
 // When leaving the ignored ones out saves at least one 256-token tile,

@@ -84,6 +84,38 @@ __device__ __forceinline__ void fold_masked(const Acc& acc, float (&m)[kNI], flo
   }
 }
 
+// The target logit: tile row r_lane + 16 i + e of column j is held by this lane
+// (r_lane = the lane's first row, 4 (lane / 16) within its wave's 128 rows).
+// rel[j] is the target's row relative to the wave's first row; the wave's
+// rows that belong to the shard are [0, wave_live) (a shard's last tile is
+// padded past its rows, and those padding rows must not be taken for the
+// next shard's ids). Each target that lies in the tile sits in exactly one
+// lane, which writes it out; the test is uniform over the wave, so waves
+// without a target skip the selection.
+__device__ __forceinline__ void capture_target(const Acc& acc, const int (&rel)[kNI], int wave_live, int lane,
+                                               float* __restrict__ yt, int row0) {
+  bool mine[kNI];
+  bool any = false;
+  const int lim = min(kWaveM, wave_live);
+#pragma unroll
+  for (int j = 0; j < kNI; ++j) {
+    mine[j] = rel[j] >= 0 && rel[j] < lim && ((rel[j] >> 2) & 3) == (lane >> 4);
+    any |= mine[j];
+  }
+  if (!__any(any)) return;
+#pragma unroll
+  for (int j = 0; j < kNI; ++j) {
+    if (!mine[j]) continue;
+    const int ii = rel[j] >> 4, ee = rel[j] & 3;
+    float y = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kMI; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y = (i == ii && e == ee) ? acc[i][j][e] : y;
+    yt[row0 + kBlk * j + (lane & 15)] = y;
+  }
+}
+
 // Fixed-order tree sum over the first 256 threads of a block (deterministic).
 __device__ __forceinline__ void block_sum256(double& a, long long& b, double* sa, long long* sb) {
   const int t = threadIdx.x;
@@ -158,15 +190,23 @@ __device__ __forceinline__ void fwd_finish_item(const FwdArgs& a, int tb, int sp
 __global__ __launch_bounds__(kThreads, 1) void fwd_round_kernel(FwdArgs a, ShardTable shards, int k_begin,
                                                                 int k_end, int first) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[kMainLds];
+  __shared__ int tgt[kBN];  // the targets of this block's tokens (-1: none)
   LCE_LDS char* lds = (LCE_LDS char*)lds_raw;
   const int wave = wave_id();
   const int lane = lane_id();
-  const int wm = wave / kWN;
+  const int wm = wave / kWN, wn = wave % kWN;
   int tb, split;
   xcd_tile(blockIdx.x, a.token_blocks, a.S, tb, split);
   const int t0 = split * a.tiles_per_split;
   const int n_my = min(t0 + a.tiles_per_split, a.n_vtiles) - t0;  // tiles per shard
   const int n_all = (k_end - k_begin) * n_my;
+  if (threadIdx.x < kBN) {  // read before the first tile's epilogue (the main loop passes barriers)
+    const int row = tb * kBN + threadIdx.x;
+    const int t = row < a.N ? a.targets[row] : -1;
+    // ignored and out-of-range targets are never captured (their yt stays 0 / NaN)
+    tgt[threadIdx.x] = (t == a.ignore_index || t < 0 || t >= a.Vs * a.P) ? -1 : t;
+  }
+  const int row0 = tb * kBN + wn * kWaveN;  // first token of this wave's columns
 
   float m[kNI], z[kNI];
 #pragma unroll
@@ -188,6 +228,16 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_round_kernel(FwdArgs a, Shard
       tile_prologue(lw, lx, a.H, lds);
     }
     const int live = a.Vs - vt * kBM;
+    // the target logits that lie in this tile (vocabulary rows of this wave:
+    // from the shard's id, the tile and the wave's half)
+    const int wave_v0 = shards.id[k_begin + i / n_my] * a.Vs + vt * kBM + wm * kWaveM;
+    int rel[kNI];
+#pragma unroll
+    for (int j = 0; j < kNI; ++j) {
+      const int t = tgt[wn * kWaveN + kBlk * j + (lane & 15)];
+      rel[j] = t < 0 ? -1 : t - wave_v0;
+    }
+    capture_target(acc, rel, live - wm * kWaveM, lane, a.yt, row0);
     if (live >= kBM)
       fold_full(acc, m, z);
     else
@@ -197,45 +247,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_round_kernel(FwdArgs a, Shard
 }
 
 // --------------------------------------------------------------------------
-// Target logit y_t = x_i . w_{t_i} (fp32 accumulation), one wave per token, read
-// from the shard that owns t_i, for the tokens whose target lies in the shards
-// [s_lo, s_hi) given (shards.p indexed by shard id). With init, first every
-// ignored token gets 0 and every other token NaN (filled in by this or a later
-// call once its shard is present): a target outside [0, V) is never filled, so
-// its token's loss, and the mean, stay NaN.
+// Before the first round: yt = 0 for ignored tokens, NaN for the others.
 // --------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void target_logit_kernel(const uint16_t* __restrict__ X, int N, int H,
-                                                           ShardTable shards, int Vs, int V, int s_lo, int s_hi,
-                                                           const int* __restrict__ targets, int ignore_index,
-                                                           float* __restrict__ yt, int init) {
-  const int lane = lane_id();
-  const int row = blockIdx.x * 4 + wave_id();
-  if (row >= N) return;
-  const int t = __builtin_amdgcn_readfirstlane(targets[row]);
-  if (t == ignore_index || t < 0 || t >= V) {
-    if (init && lane == 0) yt[row] = (t == ignore_index) ? 0.0f : __builtin_nanf("");
-    return;
-  }
-  const int s = t / Vs;
-  if (s < s_lo || s >= s_hi) {  // the target's shard is not among these
-    if (init && lane == 0) yt[row] = __builtin_nanf("");
-    return;
-  }
-  const uint16_t* w = shards.p[s] + (size_t)(t - s * Vs) * H;
-  const uint16_t* x = X + (size_t)row * H;
-  float acc = 0.0f;
-  for (int c = lane * 8; c < H; c += 512) {
-    const u32x4 xv = *reinterpret_cast<const u32x4*>(x + c);
-    const u32x4 wv = *reinterpret_cast<const u32x4*>(w + c);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc = fmaf(__uint_as_float(xv[q] << 16), __uint_as_float(wv[q] << 16), acc);
-      acc = fmaf(__uint_as_float(xv[q] & 0xffff0000u), __uint_as_float(wv[q] & 0xffff0000u), acc);
-    }
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-  if (lane == 0) yt[row] = acc;
+__global__ __launch_bounds__(256) void init_target_logits_kernel(const int* __restrict__ targets, int N,
+                                                                 int ignore_index, float* __restrict__ yt) {
+  const int row = blockIdx.x * 256 + threadIdx.x;
+  if (row < N) yt[row] = targets[row] == ignore_index ? 0.0f : __builtin_nanf("");
 }
 
 // --------------------------------------------------------------------------
@@ -767,10 +784,8 @@ hipError_t launch_finalize(const FwdArgs& a, hipStream_t st) {
   return last();
 }
 
-hipError_t launch_target_logit(const uint16_t* X, int N, int H, const ShardTable& shards, int Vs, int V, int s_lo,
-                               int s_hi, const int* targets, int ignore_index, float* yt, int init, hipStream_t st) {
-  hipLaunchKernelGGL(target_logit_kernel, dim3((N + 3) / 4), dim3(256), 0, st, X, N, H, shards, Vs, V, s_lo, s_hi,
-                     targets, ignore_index, yt, init);
+hipError_t launch_init_target_logits(const int* targets, int N, int ignore_index, float* yt, hipStream_t st) {
+  hipLaunchKernelGGL(init_target_logits_kernel, dim3((N + 255) / 256), dim3(256), 0, st, targets, N, ignore_index, yt);
   return last();
 }
 
