@@ -257,6 +257,7 @@ def materialized(hidden, shards, targets, args, out, dev):
     base = torch.cuda.memory_allocated(dev)
     x = hidden.detach().clone().requires_grad_(True)
     wp = w.clone().requires_grad_(True)
+    x_shape, w_rows = tuple(x.shape), w.shape[0]
     tl = targets.long()
     io = torch.cuda.memory_allocated(dev) - base
 
@@ -268,16 +269,31 @@ def materialized(hidden, shards, targets, args, out, dev):
         loss.backward()
         return loss
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize(dev)
-    torch.cuda.reset_peak_memory_stats(dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        loss = step()
-    e1.record()
-    torch.cuda.synchronize(dev)
+    try:
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize(dev)
+        torch.cuda.reset_peak_memory_stats(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            loss = step()
+        e1.record()
+        torch.cuda.synchronize(dev)
+    except torch.cuda.OutOfMemoryError as e:
+        # the plain path does not fit: record what it asked for
+        msg = str(e).splitlines()[0]
+        peak = torch.cuda.max_memory_allocated(dev) - base
+        x.grad = None
+        wp.grad = None
+        del x, wp, w
+        torch.cuda.empty_cache()
+        return {"what": "bf16 linear -> fp32 cross_entropy (mean, ignore_index=-100) -> autograd; bf16 gradients",
+                "out_of_memory": msg, "peak_bytes_before_failure": int(peak),
+                "device_bytes": int(torch.cuda.get_device_properties(dev).total_memory),
+                "full_logits_bf16_bytes": int(x_shape[0]) * int(w_rows) * 2,
+                "full_logits_fp32_bytes": int(x_shape[0]) * int(w_rows) * 4,
+                "lce_ms_per_step": out["ms_per_step"], "lce_transient_bytes": out["transient_bytes"]}
     ms = e0.elapsed_time(e1) / args.steps
     peak = torch.cuda.max_memory_allocated(dev) - base
     grads = x.grad.numel() * x.grad.element_size() + wp.grad.numel() * wp.grad.element_size()
@@ -431,6 +447,7 @@ def main() -> int:
 
     n, h, v = w.n_tokens, w.hidden, w.vocab
     ms_per_step = elapsed_ms / args.steps
+    executed = sum(e["flops"] for e in kernels) / args.steps  # algorithmic MFMA flops of the traced launches
     tokens_s = n / (ms_per_step / 1e3)
     flops_8 = 8.0 * n * h * v
     flops_6 = 6.0 * n * h * v
@@ -472,7 +489,13 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "n_tokens": n, "hidden": h, "vocab": v, "n_shards": w.n_shards,
                    "shard_rows": vs, "ignore_frac": w.ignore_frac, "targets": w.targets, "seed": args.seed},
+        # 8NHV counts every token, ignored ones included (the pages' work per
+        # token); the backward leaves ignored tokens out when that saves a
+        # tile, so the MFMA work executed is also reported
         "mfma_frac": round(tflops_8 / PEAK_BF16_TFLOPS, 4),
+        "executed_flops_per_step": executed,
+        "mfma_frac_executed": round(executed / (ms_per_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "valid_tokens": int(np.sum(batch.targets != -100)),
         "tflops_8nhv": round(tflops_8, 2),
         "tflops_6nhv": round(flops_6 / (ms_per_step / 1e3) / 1e12, 2),
         "peak_hbm_bytes": int(peak),

@@ -176,7 +176,8 @@ Plan make_plan(const lce_dims* d) {
   // hidden rows of the kept tokens (compact mode): all of them when that is
   // no more than two token chunks, else two token-chunk buffers that the
   // units' chunks alternate in
-  p.compact = (d->flags & LCE_FLAG_KEEP_IGNORED_ROWS) == 0;
+  // (the dX rows of kept tokens are addressed with 32-bit byte offsets)
+  p.compact = (d->flags & LCE_FLAG_KEEP_IGNORED_ROWS) == 0 && p.N * p.H * 4 < (int64_t(1) << 32);
   p.xv_whole = p.N <= 2 * p.ncs;
   p.xv_bytes = !p.compact ? 0 : p.xv_whole ? size_t(p.N) * p.H * 2 : align256(size_t(p.ncs) * p.H * 2);
   p.off_xv = o;

@@ -500,50 +500,52 @@ __device__ __forceinline__ void recompute_g_tile(const BwdGArgs& a, int id, LCE_
 
 // Stores (accumulate = 0) or adds (accumulate = 1) the fp32 tile into
 // C[row(m0 + r)][n0 + c] for r < m_valid - m0, c < n_valid - n0 (n_valid a
-// multiple of 4), where row(i) = rmap[i].row when a row map is given (the dX
-// rows of the positions) and i otherwise. The tile goes through LDS in two
-// halves of 128 rows (the rows of the waves with wm = 0, then wm = 1), so that
-// global memory sees 16-byte accesses along whole rows. For each half, a
-// thread issues all of its loads of C before the half is staged, so they fly
-// while the accumulators are written to LDS and the half costs one round trip
-// to memory. LDS row r holds the 256 floats of the row, with column c stored
-// at c ^ (16 ((r >> 2) & 3)), so the four 16-lane groups of an accumulator
-// write (rows r, r + 4, r + 8, r + 12, 16 columns each) use different banks.
-// Needs the 128 KB of LDS free (the main loop ends on a barrier).
-// Thread t handles 16-byte chunk (t & 63) of rows (t >> 6) + 8 k, k < kIt.
-template <int kIt, bool kFull>
-__device__ __forceinline__ void half_rows(const TokInfo* __restrict__ rmap, int r0, int m_valid, int (&rows)[kIt]) {
-#pragma unroll
-  for (int k = 0; k < kIt; ++k) {
-    const int gr = r0 + k * (kThreads / 64) + (threadIdx.x >> 6);
-    rows[k] = gr;
-    if (rmap && (kFull || gr < m_valid)) rows[k] = rmap[gr].row;
-  }
+// multiple of 4), where row(m0 + r) = rowmap[r] when a row map is given (the
+// dX rows of the tile's positions, staged in LDS) and m0 + r otherwise. The
+// tile goes through LDS in two halves of 128 rows (the rows of the waves with
+// wm = 0, then wm = 1), so that global memory sees 16-byte accesses along
+// whole rows. For each half, a thread issues all of its loads of C before the
+// half is staged, so they fly while the accumulators are written to LDS and
+// the half costs one round trip to memory. LDS row r holds the 256 floats of
+// the row, with column c stored at c ^ (16 ((r >> 2) & 3)), so the four
+// 16-lane groups of an accumulator write (rows r, r + 4, r + 8, r + 12, 16
+// columns each) use different banks. Needs the 128 KB of LDS free (the main
+// loop ends on a barrier). Thread t handles 16-byte chunk (t & 63) of rows
+// (t >> 6) + 8 k, k < kIt; a row's index is read again where it is used
+// rather than kept in registers across the staging. With a row map the
+// element's byte offset from C is formed in 32 bits (the host allows a row
+// map only when the whole of C is below 4 GiB), one register per access.
+__device__ __forceinline__ float* elem(float* C, int ldc, const int* rowmap, int m0, int r, int gc) {
+  if (rowmap)
+    return reinterpret_cast<float*>(reinterpret_cast<char*>(C) +
+                                    ((uint32_t)rowmap[r] * (uint32_t)ldc + (uint32_t)gc) * 4u);
+  return C + (size_t)(m0 + r) * ldc + gc;
 }
 template <int kIt, bool kFull>
-__device__ __forceinline__ void load_half(const float* __restrict__ C, int ldc, int r0, int m_valid, int n0,
-                                          int n_valid, const int (&rows)[kIt], float4 (&old)[kIt]) {
+__device__ __forceinline__ void load_half(const float* __restrict__ C, int ldc, const int* rowmap, int m0, int h,
+                                          int m_valid, int n0, int n_valid, float4 (&old)[kIt]) {
   const int c = threadIdx.x & 63;
   const int gc = n0 + 4 * c;
 #pragma unroll
   for (int k = 0; k < kIt; ++k) {
-    const int gr = r0 + k * (kThreads / 64) + (threadIdx.x >> 6);
+    const int r = 128 * h + k * (kThreads / 64) + (threadIdx.x >> 6);
     old[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    if (kFull || (gr < m_valid && gc < n_valid))
-      old[k] = *reinterpret_cast<const float4*>(C + (size_t)rows[k] * ldc + gc);
+    if (kFull || (m0 + r < m_valid && gc < n_valid))
+      old[k] = *reinterpret_cast<const float4*>(elem(const_cast<float*>(C), ldc, rowmap, m0, r, gc));
   }
 }
 template <int kIt, bool kFull, bool kAcc>
-__device__ __forceinline__ void store_half(float* __restrict__ C, int ldc, int r0, int m_valid, int n0, int n_valid,
-                                           const int (&rows)[kIt], const float* tile, const float4 (&old)[kIt]) {
+__device__ __forceinline__ void store_half(float* __restrict__ C, int ldc, const int* rowmap, int m0, int h,
+                                           int m_valid, int n0, int n_valid, const float* tile,
+                                           const float4 (&old)[kIt]) {
   const int c = threadIdx.x & 63;
   const int gc = n0 + 4 * c;
 #pragma unroll
   for (int k = 0; k < kIt; ++k) {
-    const int r = k * (kThreads / 64) + (threadIdx.x >> 6);
-    const int gr = r0 + r;
-    if (kFull || (gr < m_valid && gc < n_valid)) {
-      float4 v = *reinterpret_cast<const float4*>(tile + r * 256 + 4 * (c ^ (4 * ((r >> 2) & 3))));
+    const int rl = k * (kThreads / 64) + (threadIdx.x >> 6);  // row within the half
+    const int r = 128 * h + rl;
+    if (kFull || (m0 + r < m_valid && gc < n_valid)) {
+      float4 v = *reinterpret_cast<const float4*>(tile + rl * 256 + 4 * (c ^ (4 * ((rl >> 2) & 3))));
       if (kAcc) {
         v.x += old[k].x;
         v.y += old[k].y;
@@ -552,15 +554,14 @@ __device__ __forceinline__ void store_half(float* __restrict__ C, int ldc, int r
       }
       // non-temporal: the next add to this tile comes from a later launch
       const f32x4 nv = {v.x, v.y, v.z, v.w};
-      __builtin_nontemporal_store(nv, reinterpret_cast<f32x4*>(C + (size_t)rows[k] * ldc + gc));
+      __builtin_nontemporal_store(nv, reinterpret_cast<f32x4*>(elem(C, ldc, rowmap, m0, r, gc)));
     }
   }
 }
 
 template <bool kFull, bool kAcc>
-__device__ __forceinline__ void store_tile_impl(const Acc& acc, float* __restrict__ C, int ldc,
-                                                const TokInfo* __restrict__ rmap, int m0, int m_valid, int n0,
-                                                int n_valid, char* ldsg) {
+__device__ __forceinline__ void store_tile_impl(const Acc& acc, float* __restrict__ C, int ldc, const int* rowmap,
+                                                int m0, int m_valid, int n0, int n_valid, char* ldsg) {
   const int wave = wave_id();
   const int lane = lane_id();
   const int wm = wave / kWN, wn = wave % kWN;
@@ -568,11 +569,8 @@ __device__ __forceinline__ void store_tile_impl(const Acc& acc, float* __restric
   float* tile = reinterpret_cast<float*>(ldsg);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int r0 = m0 + 128 * h;
-    int rows[kIt];
-    half_rows<kIt, kFull>(rmap, r0, m_valid, rows);
     float4 old[kIt];
-    if (kAcc) load_half<kIt, kFull>(C, ldc, r0, m_valid, n0, n_valid, rows, old);
+    if (kAcc) load_half<kIt, kFull>(C, ldc, rowmap, m0, h, m_valid, n0, n_valid, old);
     if (wm == h) {
 #pragma unroll
       for (int i = 0; i < kMI; ++i)
@@ -587,23 +585,23 @@ __device__ __forceinline__ void store_tile_impl(const Acc& acc, float* __restric
         }
     }
     __syncthreads();
-    store_half<kIt, kFull, kAcc>(C, ldc, r0, m_valid, n0, n_valid, rows, tile, old);
+    store_half<kIt, kFull, kAcc>(C, ldc, rowmap, m0, h, m_valid, n0, n_valid, tile, old);
     __syncthreads();
   }
 }
 
-__device__ __forceinline__ void store_tile(const Acc& acc, float* __restrict__ C, int ldc,
-                                           const TokInfo* __restrict__ rmap, int m0, int m_valid, int n0,
-                                           int n_valid, int accumulate, char* ldsg) {
+// rowmap: NULL, or the LDS row map of the tile's 256 rows (see store_tile_impl).
+__device__ __forceinline__ void store_tile(const Acc& acc, float* __restrict__ C, int ldc, const int* rowmap, int m0,
+                                           int m_valid, int n0, int n_valid, int accumulate, char* ldsg) {
   const bool full = m0 + kBM <= m_valid && n0 + kBN <= n_valid;
   if (full && accumulate)
-    store_tile_impl<true, true>(acc, C, ldc, rmap, m0, m_valid, n0, n_valid, ldsg);
+    store_tile_impl<true, true>(acc, C, ldc, rowmap, m0, m_valid, n0, n_valid, ldsg);
   else if (full)
-    store_tile_impl<true, false>(acc, C, ldc, rmap, m0, m_valid, n0, n_valid, ldsg);
+    store_tile_impl<true, false>(acc, C, ldc, rowmap, m0, m_valid, n0, n_valid, ldsg);
   else if (accumulate)
-    store_tile_impl<false, true>(acc, C, ldc, rmap, m0, m_valid, n0, n_valid, ldsg);
+    store_tile_impl<false, true>(acc, C, ldc, rowmap, m0, m_valid, n0, n_valid, ldsg);
   else
-    store_tile_impl<false, false>(acc, C, ldc, rmap, m0, m_valid, n0, n_valid, ldsg);
+    store_tile_impl<false, false>(acc, C, ldc, rowmap, m0, m_valid, n0, n_valid, ldsg);
 }
 
 // The K loop of a gradient tile runs over the live part of its contraction
@@ -613,7 +611,7 @@ __device__ __forceinline__ void store_tile(const Acc& acc, float* __restrict__ C
 // clamped to the last existing one). A dW tile with nothing to contract
 // writes zeros (or, accumulating, leaves its rows as they are); a dX tile
 // past the existing positions has no rows to write.
-__device__ __forceinline__ void grad_tile(const GradArgs& a, int id, LCE_LDS char* lds, char* ldsg) {
+__device__ __forceinline__ void grad_tile(const GradArgs& a, int id, LCE_LDS char* lds, char* ldsg, int* rowmap) {
   const int wave = wave_id();
   const int lane = lane_id();
   const int dx_rows = a.nc_pad / kBM, dw_rows = a.vc_pad / kBM;
@@ -632,12 +630,21 @@ __device__ __forceinline__ void grad_tile(const GradArgs& a, int id, LCE_LDS cha
   Acc acc;
   if (is_dx) {
     if (tm * kBM >= nv) return;
+    // the dX rows of the tile's positions, staged in LDS while the main loop
+    // runs (its barriers order these writes before the epilogue's reads)
+    const bool mapped = a.prep->compact;
+    if (mapped && threadIdx.x < kBM) {
+      const int pos = tm * kBM + threadIdx.x;
+      rowmap[threadIdx.x] = pos < nv ? a.tinfo[a.n0 + pos].row : 0;
+    }
     KContigLoader la;
     KMajorLoader lb;
     la.init(a.G, a.ldg, tm * kBM, nv, wave, lane);
     lb.init(a.Wc, a.H, tn * kBN, a.H, a.vc, wave, lane);
     tile_mainloop<false, true>(la, lb, (a.vc + kBK - 1) / kBK * kBK, lds, acc);
-    store_tile(acc, a.dX, a.H, a.tinfo + a.n0, tm * kBM, nv, tn * kBN, a.H, a.acc_dx, ldsg);
+    // without a row map position n0 + i is row n0 + i
+    store_tile(acc, mapped ? a.dX : a.dX + (size_t)a.n0 * a.H, a.H, mapped ? rowmap : nullptr, tm * kBM, nv,
+               tn * kBN, a.H, a.acc_dx, ldsg);
   } else {
     if (nv <= 0) {
       if (a.acc_dw) return;
@@ -660,10 +667,11 @@ __device__ __forceinline__ void grad_tile(const GradArgs& a, int id, LCE_LDS cha
 __global__ __launch_bounds__(kThreads, 1) void bwd_step_kernel(GradArgs gr, int grad_slots, BwdGArgs bg,
                                                                int g_tiles) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[kMainLds];
+  __shared__ int rowmap[kBM];
   LCE_LDS char* lds = (LCE_LDS char*)lds_raw;
   const int id = blockIdx.x;
   if (id < grad_slots) {
-    grad_tile(gr, id, lds, lds_raw);
+    grad_tile(gr, id, lds, lds_raw, rowmap);
   } else if (id - grad_slots < g_tiles) {
     recompute_g_tile(bg, id - grad_slots, lds, lds_raw);
   }
