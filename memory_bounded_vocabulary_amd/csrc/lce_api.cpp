@@ -387,10 +387,9 @@ std::vector<Unit> backward_units(const Plan& p, const int32_t* ids, int n_ids, c
 }
 
 // Token info of the positions the backward runs over (kept tokens only when
-// that saves a token tile) and the loss scale; then, in compact mode, zero
-// the ignored rows of `dx_zero` (NULL: leave them, when accumulating).
+// that saves a token tile) and the loss scale.
 int run_bwd_prep(const Plan& p, const lce_dims* d, const int32_t* targets, const float* lse, const float* dloss,
-                 float* dx_zero, char* ws, hipStream_t s) {
+                 char* ws, hipStream_t s) {
   lce::BwdPrep* prep = reinterpret_cast<lce::BwdPrep*>(ws + p.off_prep);
   lce::TokInfo* tinfo = reinterpret_cast<lce::TokInfo*>(ws + p.off_tinfo);
   int st = hip_status(traced(kBwdPrep, Work(0.0, 4.0 * double(p.N) + 16.0 * double(p.N)), s,
@@ -399,13 +398,7 @@ int run_bwd_prep(const Plan& p, const lce_dims* d, const int32_t* targets, const
                                                            d->reduction, p.compact ? 1 : 0, prep, tinfo, s);
                              }),
                       "backward preparation");
-  if (st || !dx_zero) return st;
-  return hip_status(traced(kGather, Work(0.0, 0.0), s,
-                           [&] {
-                             return lce::launch_zero_ignored_rows(dx_zero, prep, targets, int(p.N), int(p.H),
-                                                                  d->ignore_index, s);
-                           }),
-                    "zero ignored rows");
+  return st;
 }
 
 int run_convert(bool widen, const void* src, void* dst, int64_t rows, int64_t cols, hipStream_t s) {
@@ -428,18 +421,26 @@ int run_convert(bool widen, const void* src, void* dst, int64_t rows, int64_t co
 // from a gathered copy: all positions in one buffer when they fit
 // (xv_whole), else two chunk buffers; a unit whose chunk is not in a buffer
 // gets it gathered, before its recompute launch, into the buffer the
-// previous unit does not use (whose GEMMs run in that same launch).
-int run_bwd_units(const Plan& p, const lce_dims* d, const std::vector<Unit>& units, const uint16_t* X, float* dX,
-                  bool acc_dw, char* ws, hipStream_t s) {
+// previous unit does not use (whose GEMMs run in that same launch). The first
+// gather also zeroes the ignored tokens' rows of `dx_zero` (NULL: leave them,
+// when accumulating): in compact mode no contraction writes them.
+int run_bwd_units(const Plan& p, const lce_dims* d, const std::vector<Unit>& units, const uint16_t* X,
+                  const int32_t* targets, float* dX, float* dx_zero, bool acc_dw, char* ws, hipStream_t s) {
   const double dH = double(p.H);
   auto gbuf = [&](size_t u) { return reinterpret_cast<uint16_t*>(ws + p.off_g + (u & 1) * p.g_bytes); };
   float* dw32 = reinterpret_cast<float*>(ws + p.off_dw32);
   const lce::BwdPrep* prep = reinterpret_cast<const lce::BwdPrep*>(ws + p.off_prep);
   const lce::TokInfo* tinfo = reinterpret_cast<const lce::TokInfo*>(ws + p.off_tinfo);
   uint16_t* xv_base = reinterpret_cast<uint16_t*>(ws + p.off_xv);
+  bool zero_pending = dx_zero != nullptr;
   auto gather = [&](uint16_t* dst, int n0, int nc) {
+    float* z = zero_pending ? dx_zero : nullptr;
+    zero_pending = false;
     return hip_status(traced(kGather, Work(0.0, 4.0 * double(nc) * dH), s,
-                             [&] { return lce::launch_gather_rows(X, dst, prep, tinfo, n0, nc, int(p.H), s); }),
+                             [&] {
+                               return lce::launch_gather_rows(X, dst, prep, tinfo, n0, nc, int(p.H), z, targets,
+                                                              int(p.N), d->ignore_index, s);
+                             }),
                       "gather rows");
   };
   // the gathered rows of each unit's positions
@@ -778,7 +779,7 @@ int lce_backward(const lce_dims* d, const void* hidden, const void* const* w_sha
     st = run_convert(true, d_hidden, dx32, p.N, p.H, s);
     if (st) return st;
   }
-  st = run_bwd_prep(p, d, targets, lse, dloss, acc_dx ? nullptr : dx32, ws, s);
+  st = run_bwd_prep(p, d, targets, lse, dloss, ws, s);
   if (st) return st;
   const void* w_by_round[LCE_MAX_SHARDS];
   void* dw_by_round[LCE_MAX_SHARDS];
@@ -787,7 +788,8 @@ int lce_backward(const lce_dims* d, const void* hidden, const void* const* w_sha
     dw_by_round[k] = d_w_shards[order[k]];
   }
   const std::vector<Unit> units = backward_units(p, order, d->n_shards, w_by_round, dw_by_round, ws, acc_dx, acc_dw);
-  st = run_bwd_units(p, d, units, static_cast<const uint16_t*>(hidden), dx32, acc_dw, ws, s);
+  st = run_bwd_units(p, d, units, static_cast<const uint16_t*>(hidden), targets, dx32, acc_dx ? nullptr : dx32, acc_dw,
+                     ws, s);
   if (st || !p.bf16_grads) return st;
   return run_convert(false, dx32, d_hidden, p.N, p.H, s);
 }
@@ -852,13 +854,14 @@ int lce_bwd_round(const lce_dims* d, int round, int shard_index, const void* hid
     st = run_convert(true, d_hidden, dx32, p.N, p.H, s);
     if (st) return st;
   }
-  st = run_bwd_prep(p, d, targets, lse, dloss, acc_dx ? nullptr : dx32, ws, s);
+  st = run_bwd_prep(p, d, targets, lse, dloss, ws, s);
   if (st) return st;
   const int32_t id = shard_index;
   const void* w_one[1] = {w_shard};
   void* dw_one[1] = {d_w_shard};
   const std::vector<Unit> units = backward_units(p, &id, 1, w_one, dw_one, ws, acc_dx, acc_dw);
-  st = run_bwd_units(p, d, units, static_cast<const uint16_t*>(hidden), dx32, acc_dw, ws, s);
+  st = run_bwd_units(p, d, units, static_cast<const uint16_t*>(hidden), targets, dx32, acc_dx ? nullptr : dx32, acc_dw,
+                     ws, s);
   if (st || !p.bf16_grads || round != d->n_shards - 1) return st;
   return run_convert(false, dx32, d_hidden, p.N, p.H, s);
 }

@@ -61,13 +61,11 @@ struct TokInfo {
 hipError_t launch_bwd_prep(const int* targets, const float* lse, int N, int ignore_index, const float* dloss,
                            int reduction, int allow_compact, BwdPrep* prep, TokInfo* tinfo, hipStream_t st);
 // Compact mode only (else it does nothing): xv[i] = X[tinfo[n0 + i].row] for
-// the positions n0 + i < min(n0 + nc, n_eff).
+// the positions n0 + i < min(n0 + nc, n_eff); and, when dX is non-NULL, zero
+// the rows of dX [N][H] fp32 whose target is ignore_index (the contractions
+// never write them in compact mode).
 hipError_t launch_gather_rows(const uint16_t* X, uint16_t* xv, const BwdPrep* prep, const TokInfo* tinfo, int n0,
-                              int nc, int H, hipStream_t st);
-// Compact mode only: zero the rows of dX [N][H] fp32 whose target is
-// ignore_index (the contractions never write them in compact mode).
-hipError_t launch_zero_ignored_rows(float* dX, const BwdPrep* prep, const int* targets, int N, int H,
-                                    int ignore_index, hipStream_t st);
+                              int nc, int H, float* dX, const int* targets, int N, int ignore_index, hipStream_t st);
 // Recompute + G of one backward unit (shard, vocabulary chunk, token chunk).
 // Token indices n0, nc are positions (see BwdPrep).
 struct BwdGArgs {

@@ -307,16 +307,26 @@ __global__ __launch_bounds__(1024) void bwd_prep_kernel(const int* __restrict__ 
   if (reduction == 0) gscale = (float)((double)dloss[0] / (double)n_valid);  // NaN / inf if n_valid = 0: unused then
   if (reduction == 1) gscale = dloss[0];
   int pos = compact ? wave_base[wave] + incl - cnt : r0;
-  for (r = r0; r < r1; ++r) {
-    const int tg = targets[r];
-    if (compact && tg == ignore_index) continue;
+  auto put = [&](int row, int tg, float l, float g) {
+    if (compact && tg == ignore_index) return;
     TokInfo ti;
-    ti.lse = lse[r];
+    ti.lse = l;
     ti.target = tg;
-    ti.g = reduction == 2 ? dloss[r] : gscale;
-    ti.row = r;
+    ti.g = g;
+    ti.row = row;
     tinfo[pos++] = ti;
+  };
+  for (r = r0; r + 4 <= r1; r += 4) {  // 16-byte loads of four tokens at a time
+    const int4 tg = *reinterpret_cast<const int4*>(targets + r);
+    const float4 l = *reinterpret_cast<const float4*>(lse + r);
+    float4 g = make_float4(gscale, gscale, gscale, gscale);
+    if (reduction == 2) g = *reinterpret_cast<const float4*>(dloss + r);
+    put(r, tg.x, l.x, g.x);
+    put(r + 1, tg.y, l.y, g.y);
+    put(r + 2, tg.z, l.z, g.z);
+    put(r + 3, tg.w, l.w, g.w);
   }
+  for (; r < r1; ++r) put(r, targets[r], lse[r], reduction == 2 ? dloss[r] : gscale);
   if (t == 0) {
     BwdPrep p;
     p.n_valid = n_valid;
@@ -328,10 +338,14 @@ __global__ __launch_bounds__(1024) void bwd_prep_kernel(const int* __restrict__ 
 }
 
 // Compact mode: copy the hidden rows of positions [n0, n0 + nc) (those that
-// exist) into xv, one block per row, 16-byte accesses.
+// exist) into xv, one block per row, 16-byte accesses; and, when dX is given,
+// zero the dX [N][H] rows of ignored tokens (the contractions never write
+// them in compact mode).
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __restrict__ X, uint16_t* __restrict__ xv,
                                                           const BwdPrep* __restrict__ prep,
-                                                          const TokInfo* __restrict__ tinfo, int n0, int nc, int H) {
+                                                          const TokInfo* __restrict__ tinfo, int n0, int nc, int H,
+                                                          float* __restrict__ dX, const int* __restrict__ targets,
+                                                          int N, int ignore_index) {
   if (!prep->compact) return;
   const int nv = min(nc, prep->n_eff - n0);
   const int c8 = H >> 3;
@@ -340,14 +354,7 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __rest
     u32x4* dst = reinterpret_cast<u32x4*>(xv + (size_t)i * H);
     for (int c = threadIdx.x; c < c8; c += 256) dst[c] = src[c];
   }
-}
-
-// Compact mode: zero the dX rows of ignored tokens, one block per row.
-__global__ __launch_bounds__(256) void zero_ignored_rows_kernel(float* __restrict__ dX,
-                                                                const BwdPrep* __restrict__ prep,
-                                                                const int* __restrict__ targets, int N, int H,
-                                                                int ignore_index) {
-  if (!prep->compact) return;
+  if (!dX) return;
   const int c4 = H >> 2;
   const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int r = blockIdx.x; r < N; r += gridDim.x) {
@@ -805,16 +812,11 @@ hipError_t launch_bwd_prep(const int* targets, const float* lse, int N, int igno
 }
 
 hipError_t launch_gather_rows(const uint16_t* X, uint16_t* xv, const BwdPrep* prep, const TokInfo* tinfo, int n0,
-                              int nc, int H, hipStream_t st) {
-  const int blocks = nc < 2048 ? (nc < 1 ? 1 : nc) : 2048;  // grid-stride over rows beyond that
-  hipLaunchKernelGGL(gather_rows_kernel, dim3(blocks), dim3(256), 0, st, X, xv, prep, tinfo, n0, nc, H);
-  return last();
-}
-
-hipError_t launch_zero_ignored_rows(float* dX, const BwdPrep* prep, const int* targets, int N, int H,
-                                    int ignore_index, hipStream_t st) {
-  const int blocks = N < 2048 ? (N < 1 ? 1 : N) : 2048;
-  hipLaunchKernelGGL(zero_ignored_rows_kernel, dim3(blocks), dim3(256), 0, st, dX, prep, targets, N, H, ignore_index);
+                              int nc, int H, float* dX, const int* targets, int N, int ignore_index, hipStream_t st) {
+  const int rows = dX ? (nc > N ? nc : N) : nc;
+  const int blocks = rows < 2048 ? (rows < 1 ? 1 : rows) : 2048;  // grid-stride over rows beyond that
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(blocks), dim3(256), 0, st, X, xv, prep, tinfo, n0, nc, H, dX, targets,
+                     N, ignore_index);
   return last();
 }
 
