@@ -451,7 +451,7 @@ __device__ __forceinline__ void recompute_g_tile(const BwdGArgs& a, int id, LCE_
   // load addresses formed at each issue (as in the forward): with the two
   // K-contiguous operands this loop runs about 10 % faster than with the
   // addresses hoisted out of it
-  tile_mainloop<false, false, false, true>(lw, lx, a.H, lds, acc);
+  tile_mainloop<false, false, false, true>(lw, lx, a.H, lds, acc, a.vc - tv * kBM <= kWaveM);
 
   float lse2[kNI], g[kNI];
   int tcol[kNI];
@@ -648,7 +648,7 @@ __device__ __forceinline__ void grad_tile(const GradArgs& a, int id, LCE_LDS cha
     KMajorLoader lb;
     la.init(a.G, a.ldg, tm * kBM, nv, wave, lane);
     lb.init(a.Wc, a.H, tn * kBN, a.H, a.vc, wave, lane);
-    tile_mainloop<false, true>(la, lb, (a.vc + kBK - 1) / kBK * kBK, lds, acc);
+    tile_mainloop<false, true>(la, lb, (a.vc + kBK - 1) / kBK * kBK, lds, acc, nv - tm * kBM <= kWaveM);
     // without a row map position n0 + i is row n0 + i
     store_tile(acc, mapped ? a.dX : a.dX + (size_t)a.n0 * a.H, a.H, mapped ? rowmap : nullptr, tm * kBM, nv,
                tn * kBN, a.H, a.acc_dx, ldsg);
@@ -665,7 +665,7 @@ __device__ __forceinline__ void grad_tile(const GradArgs& a, int id, LCE_LDS cha
       KMajorLoader la, lb;
       la.init(a.G, a.ldg, tm * kBM, a.vc_pad, k_live, wave, lane);
       lb.init(xs, a.H, tn * kBN, a.H, nv, wave, lane);
-      tile_mainloop<true, true>(la, lb, k_live, lds, acc);
+      tile_mainloop<true, true>(la, lb, k_live, lds, acc, a.vc - tm * kBM <= kWaveM);
     }
     store_tile(acc, a.dW, a.H, nullptr, tm * kBM, a.vc, tn * kBN, a.H, a.acc_dw, ldsg);
   }

@@ -330,8 +330,18 @@ __device__ __forceinline__ void tile_prologue(const LA& la, const LB& lb, int K,
 // load into LDS is in flight, so both LDS stages are free for the caller (the
 // discarded reads of the last stage may still be in flight: they read, never
 // write, and nothing uses what they return).
+//
+// idle (uniform over the wave): the caller discards every row of this wave's
+// 128 x 64 sub-tile (a tile past the end of A's valid rows, such as a shard's
+// last vocabulary tile with at most 128 live rows, in the waves with wm = 1).
+// Such a wave reads no fragments and issues no MFMA; its accumulators stay
+// zero, and it passes the same barriers as the others (one before the loop,
+// one per stage). Only waves with wm = 1 may be idle, and those never issue
+// loads (the loading waves are waves 0 .. kLoadWaves - 1, all with wm = 0).
 template <bool A_KMAJ, bool B_KMAJ, bool kIssued = false, bool kOpaque = false, class LA, class LB>
-__device__ __forceinline__ void tile_mainloop(const LA& la, const LB& lb, int K, LCE_LDS char* lds, Acc& acc) {
+__device__ __forceinline__ void tile_mainloop(const LA& la, const LB& lb, int K, LCE_LDS char* lds, Acc& acc,
+                                              bool idle = false) {
+  static_assert(kLoadWaves <= kWN, "loading waves must all have wm = 0");
   const int wave = wave_id();
   const int lane = lane_id();
   const int wm = wave / kWN, wn = wave % kWN;
@@ -345,6 +355,12 @@ __device__ __forceinline__ void tile_mainloop(const LA& la, const LB& lb, int K,
     for (int j = 0; j < kNI; ++j) acc[i][j] = f32x4{};
   const int kt_n = K / kBK;
   if (!kIssued) tile_prologue(la, lb, K, lds);
+  // a scalar branch (the condition is made uniform explicitly), so a wave that
+  // does not take it never runs these barriers with its lanes masked off
+  if (__builtin_amdgcn_readfirstlane(idle && wm == 1 ? 1 : 0)) {
+    for (int kt = 0; kt <= kt_n; ++kt) __syncthreads();
+    return;
+  }
   if (kt_n > 1)
     wait_vm<2 * kLoadJ>();  // stage 0 landed (the loads of stage 1 may still fly)
   else
