@@ -9,8 +9,10 @@ one JSON line: tokens/s over the K timed steps, the fraction of MI355X dense
 bf16 MFMA peak the step reaches, peak device bytes, a roofline figure for the
 kernel with the largest share of the step (durations from HIP events recorded
 around every launch on the launching stream, in a second pass of K steps),
-the forward / backward split per step (median and min), and the CPU oracle
-timed on a bounded sample of the same workload on the host cores.
+the forward / backward split per step (median and min), the same step and
+torch's bf16 GEMM on random and on all-zero data (the chip's power limit makes
+the MFMA rate depend on the data), and the CPU oracle timed on a bounded
+sample of the same workload on the host cores.
 """
 from __future__ import annotations
 
@@ -242,6 +244,87 @@ def variants(lce, hidden, shards, targets, d_hidden, d_shards, dloss, args, out,
     return res
 
 
+def power_context(lce, hidden, shards, targets, ws, dloss, d_hidden, d_shards, dev, window_ms: float = 300.0):
+    """How far the chip's power limit, rather than the schedule, sets the MFMA
+    rate. The same step of this library, on the workload's random inputs and
+    on all-zero inputs of the same shapes (same targets, same launches, same
+    memory traffic; only the bits the MFMA pipes and the data paths toggle
+    differ), alternated random / zero / random / zero; and torch's bf16 GEMM
+    (hipBLASLt) at 8192^3 on random N(0, 1) operands and on zeros. Each entry
+    gives the rate as a fraction of the published dense bf16 peak and the
+    shader clock sampled meanwhile (each measurement repeats its step for
+    about window_ms, at least 3 times, so the driver's clock average covers it)."""
+    import torch
+    n, h = hidden.shape
+    v = len(shards) * shards[0].shape[0]
+    zx = torch.zeros_like(hidden)
+    zw = [torch.zeros_like(s) for s in shards]
+
+    def one(x, w, e):
+        e[0].record()
+        _, lse = lce.forward(x, w, targets, workspace=ws)
+        e[1].record()
+        lce.backward(x, w, targets, lse, dloss, workspace=ws, d_hidden=d_hidden, d_shards=d_shards)
+        e[2].record()
+
+    def lib(x, w):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        one(x, w, e)  # warm-up, and the step's length
+        torch.cuda.synchronize(dev)
+        reps = max(3, min(400, int(window_ms / max(e[0].elapsed_time(e[2]), 1e-3)) + 1))
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+        with ClockSampler(sclk_reader(0)) as clk:
+            for e in ev:
+                one(x, w, e)
+            torch.cuda.synchronize(dev)
+        fwd = sum(e[0].elapsed_time(e[1]) for e in ev) / reps
+        bwd = sum(e[1].elapsed_time(e[2]) for e in ev) / reps
+        c = clk.summary()
+        return {"reps": reps, "fwd_ms": round(fwd, 4), "bwd_ms": round(bwd, 4),
+                "fwd_frac": round(2.0 * n * h * v / (fwd / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "step_frac_8nhv": round(8.0 * n * h * v / ((fwd + bwd) / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "sclk_median_mhz": c["median_mhz"] if c else None}
+
+    runs = {"random": [], "zeros": []}
+    for _ in range(2):
+        runs["random"].append(lib(hidden, shards))
+        runs["zeros"].append(lib(zx, zw))
+    del zx, zw
+
+    def best(rs):
+        return min(rs, key=lambda r: r["fwd_ms"] + r["bwd_ms"])
+
+    m = 8192
+    g = torch.Generator(device=dev)
+    g.manual_seed(1)
+    a = torch.randn((m, m), device=dev, dtype=torch.float32, generator=g).to(torch.bfloat16)
+    b = torch.randn((m, m), device=dev, dtype=torch.float32, generator=g).to(torch.bfloat16)
+    za, zb = torch.zeros_like(a), torch.zeros_like(b)
+    c = torch.empty_like(a)
+
+    def gemm(x, y, iters=400):
+        for _ in range(10):
+            torch.mm(x, y, out=c)
+        torch.cuda.synchronize(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with ClockSampler(sclk_reader(0)) as clk:
+            e0.record()
+            for _ in range(iters):
+                torch.mm(x, y, out=c)
+            e1.record()
+            torch.cuda.synchronize(dev)
+        ms = e0.elapsed_time(e1) / iters
+        cs = clk.summary()
+        tf = 2.0 * m * m * m / (ms / 1e3) / 1e12
+        return {"ms": round(ms, 4), "tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                "sclk_median_mhz": cs["median_mhz"] if cs else None}
+
+    res = {"library_step_random": best(runs["random"]), "library_step_zeros": best(runs["zeros"]),
+           "hipblaslt_gemm_8192_random": gemm(a, b), "hipblaslt_gemm_8192_zeros": gemm(za, zb)}
+    del a, b, za, zb, c
+    return res
+
+
 def materialized(hidden, shards, targets, args, out, dev):
     """The plain path the method replaces, on the same inputs: the full logits
     from a bf16 linear layer, cast to fp32, torch's cross-entropy (mean over
@@ -330,6 +413,8 @@ def main() -> int:
     ap.add_argument("--compare-materialized", action="store_true",
                     help="also time the plain materialising path (bf16 linear, fp32 cross-entropy, autograd) on "
                          "the same inputs and report its step time and peak bytes beside this library's")
+    ap.add_argument("--no-power-context", action="store_true",
+                    help="skip the random-vs-zero-data comparison (library step and hipBLASLt GEMM)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="copy this many MiB device-to-device once before timing (a plain copy of known size, "
                          "for scaling hardware byte counters)")
@@ -517,6 +602,9 @@ def main() -> int:
     if args.variants:
         print("[bench] timing the per-round and bf16-gradient variants", file=sys.stderr, flush=True)
         out["variants"] = variants(lce, hidden, shards, targets, d_hidden, d_shards, dloss, args, out, dev)
+    if not args.no_power_context:
+        print("[bench] timing the step and a library GEMM on random and on zero data", file=sys.stderr, flush=True)
+        out["power_context"] = power_context(lce, hidden, shards, targets, ws, dloss, d_hidden, d_shards, dev)
     if args.compare_materialized:
         print("[bench] timing the materialising path", file=sys.stderr, flush=True)
         out["materialized"] = materialized(hidden, shards, targets, args, out, dev)
