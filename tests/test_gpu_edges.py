@@ -37,6 +37,10 @@ SHAPES = [
     ("ignored tokens left out", 1000, 128, 3000, 3, 0.3, 0.1),
     ("half ignored, empty second token chunk", 24000, 64, 2 * 20000, 2, 0.5, 0.3),
     ("large logits", 333, 512, 2048, 2, 0.1, 0.5),
+    # the backward's last vocabulary and token tiles with exactly 128 live rows
+    # (the waves of rows 128-255 skip their MFMAs) and with 129 (they do not)
+    ("last tiles with 128 live rows", 384, 128, 2 * 384, 2, 0.0, 0.05),
+    ("last tiles with 129 live rows", 385, 128, 2 * 385, 2, 0.0, 0.05),
 ]
 
 
