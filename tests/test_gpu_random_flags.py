@@ -1,7 +1,8 @@
 """GPU parity on seeded random shapes crossed with the backward's options:
 token counts and shard sizes drawn near the 256-row tile edges (127, 128,
 129, 255, 256 past a multiple of 256) or at random, ignore fractions up to
-0.9, mean or sum, random shard orders, and at random: every token kept in
+0.9, mean, sum or per-token losses (random dloss per token), random shard
+orders, and at random: every token kept in
 the backward (LCE_FLAG_KEEP_IGNORED_ROWS), accumulation into prior
 gradients (LCE_FLAG_ACCUMULATE_DX / _DW), bf16 gradient outputs
 (LCE_FLAG_BF16_GRADS). Checked against the oracle at the gate; with bf16
@@ -33,7 +34,7 @@ def _cases(n_cases=100, seed=31337):
         vs, n = _rows(rng, 2000), _rows(rng, 3000)
         h = 64 * int(rng.integers(1, 13))
         opts = dict(ign=float(rng.choice([0.0, 0.1, 0.5, 0.9])), std=float(rng.choice([0.02, 0.1, 0.5])),
-                    red=str(rng.choice(["mean", "sum"])), keep=bool(rng.random() < 0.3),
+                    red=str(rng.choice(["mean", "sum", "none"])), keep=bool(rng.random() < 0.3),
                     acc=bool(rng.random() < 0.3), bf16=bool(rng.random() < 0.3),
                     order=[int(x) for x in rng.permutation(p)] if rng.random() < 0.5 else None)
         out.append((f"case{i}: N={n} H={h} V/P={vs} P={p}", n, h, vs, p, opts))
@@ -54,7 +55,13 @@ def test_random_shape_and_flags_parity(case):
     b = workloads.make(w, seed=3 * n + h + vs)
     hidden, shards, targets = to_device(b)
     loss, lse, tl = lce.forward(hidden, shards, targets, order=o["order"], reduction=o["red"], token_loss=True)
-    dloss = torch.tensor(0.75, dtype=torch.float32, device="cuda")
+    if o["red"] == "none":
+        dl_ref = np.random.default_rng(n + h).standard_normal(n).astype(np.float32) * 0.5
+        dloss = torch.from_numpy(dl_ref).cuda()
+        dl_ref = dl_ref.astype(np.float64)
+    else:
+        dl_ref = 0.75
+        dloss = torch.tensor(0.75, dtype=torch.float32, device="cuda")
     gdt = torch.bfloat16 if o["bf16"] else torch.float32
     kw, px, pw = {}, None, None
     if o["acc"]:
@@ -68,10 +75,10 @@ def test_random_shape_and_flags_parity(case):
                            keep_ignored_rows=o["keep"], grad_dtype=gdt, **kw)
     torch.cuda.synchronize()
     ref = oracle.cross_entropy(oracle.bf16_to_f64(b.hidden), oracle.bf16_to_f64(b.weight), b.targets,
-                               reduction=o["red"], dloss=0.75)
+                               reduction=o["red"], dloss=dl_ref)
     f64 = lambda t: t.float().cpu().numpy().astype(np.float64)
     got_dx, got_dw = f64(dx), np.concatenate([f64(g) for g in dws])
-    loss_tol = 2e-3 * (max(1.0, abs(ref.loss) / 10) if o["red"] == "sum" else 1.0)
+    loss_tol = 2e-3 * (max(1.0, abs(ref.loss) / 10) if o["red"] != "mean" else 1.0)
     gpu = {"loss": float(loss.item()), "lse": f64(lse), "token_loss": f64(tl)}
     if o["acc"] and o["bf16"]:
         # the stored value is bf16(prior + gradient): compare the sum, with one bf16 rounding of it allowed
