@@ -39,6 +39,7 @@ namespace {
 constexpr int64_t kTile = 256;
 constexpr int64_t kGChunkElems = int64_t(1) << 27;  // bf16 elements of one G chunk (256 MiB)
 constexpr int64_t kVocabChunkMax = 16384;           // vocabulary rows per backward chunk
+constexpr size_t kGCachedBytes = size_t(64) << 20;  // G chunks up to this size are stored cacheable
 constexpr int kMaxSplits = 16;             // forward vocabulary splits per shard
 constexpr int kTargetWorkgroups = 256;     // one per compute unit
 constexpr int kKnownFlags =
@@ -527,6 +528,9 @@ int run_bwd_units(const Plan& p, const lce_dims* d, const std::vector<Unit>& uni
       ba.vocab_base = int(u.sh * p.Vs + u.v0);
       ba.V = int(p.V);
       ba.ldg = u.vc_pad;
+      // G chunks up to a quarter of the 256 MB last-level cache stay cached
+      // for the next launch's reads
+      ba.g_cached = size_t(u.nc_pad) * size_t(u.vc_pad) * 2 <= kGCachedBytes ? 1 : 0;
       // per position: the recompute, its X row, its G row, its token info;
       // fixed: the W chunk
       const double dvc = u.vc;

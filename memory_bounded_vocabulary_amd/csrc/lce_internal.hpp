@@ -77,6 +77,7 @@ struct BwdGArgs {
   uint16_t* G;              // [nc_pad][vc_pad], pitch ldg
   int H, Vs, v0, vc, n0, nc, nc_pad, vc_pad;
   int ignore_index, vocab_base, V, ldg;
+  int g_cached;             // 1: G stored normally (it fits the last-level cache), 0: non-temporally
   int n_tt, n_tv;           // set by the launcher
 };
 

@@ -495,13 +495,25 @@ __device__ __forceinline__ void recompute_g_tile(const BwdGArgs& a, int id, LCE_
   }
   __syncthreads();
   uint16_t* gt = a.G + (size_t)tt * kBN * a.ldg + (size_t)tv * kBM;
+  // G is read back by the next launch, from other XCDs' L2s: a chunk that
+  // fits the last-level cache is stored normally, so that it is read from
+  // there; a larger one non-temporally
+  if (a.g_cached) {
 #pragma unroll 4
-  for (int it = 0; it < kBN * kBM / 8 / kThreads; ++it) {
-    const int q = it * kThreads + threadIdx.x;
-    const int r = q >> 5, c = q & 31;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(ldsg + r * 512 + ((c ^ (r & 31)) << 4));
-    // non-temporal: G is read back by the next launch, from other XCDs' L2s
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(gt + (size_t)r * a.ldg + c * 8));
+    for (int it = 0; it < kBN * kBM / 8 / kThreads; ++it) {
+      const int q = it * kThreads + threadIdx.x;
+      const int r = q >> 5, c = q & 31;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ldsg + r * 512 + ((c ^ (r & 31)) << 4));
+      *reinterpret_cast<u32x4*>(gt + (size_t)r * a.ldg + c * 8) = v;
+    }
+  } else {
+#pragma unroll 4
+    for (int it = 0; it < kBN * kBM / 8 / kThreads; ++it) {
+      const int q = it * kThreads + threadIdx.x;
+      const int r = q >> 5, c = q & 31;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ldsg + r * 512 + ((c ^ (r & 31)) << 4));
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(gt + (size_t)r * a.ldg + c * 8));
+    }
   }
 }
 
