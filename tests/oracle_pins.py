@@ -21,7 +21,9 @@ What each check pins, and where the fact comes from:
   bias 127, 7 fraction bits; subnormals at exponent field 0; all-ones exponent
   for infinities and NaN) evaluated with math.ldexp, and against torch's
   bfloat16 -> float64 conversion; plus hand-checked patterns.
-* invariants: softmax-minus-one-hot rows sum to 0 (so sum_v dW_v = 0);
+* invariants: softmax-minus-one-hot rows sum to 0, token by token (a
+  hidden feature that is 0 in X and 1 in W reads the sum) and so
+  sum_v dW_v = 0;
   adding one vector c to every vocabulary row leaves loss and gradients
   unchanged; an ignored row contributes nothing (equal to dropping it while
   keeping n_valid); mean * n_valid = sum; the pages' ring fold over any shard
@@ -235,6 +237,13 @@ def check_invariants(orc, seed=5):
     base = orc.cross_entropy(x, w, t)
     # rows of softmax - onehot sum to zero, so the vocabulary rows of dW sum to zero
     assert np.max(np.abs(base.d_weight.sum(axis=0))) <= 1e-14 * max(1.0, np.max(np.abs(base.d_weight)) * v)
+    # the same, token by token: a feature that is 0 in every hidden row and 1 in
+    # every vocabulary row leaves the logits unchanged, and its column of dX is
+    # then each token's sum of dloss/dlogits over the vocabulary
+    aug = orc.cross_entropy(np.hstack([x, np.zeros((n, 1))]), np.hstack([w, np.ones((v, 1))]), t)
+    assert abs(aug.loss - base.loss) <= 1e-13 * max(1.0, abs(base.loss))
+    assert np.max(np.abs(aug.d_hidden[:, h])) <= 1e-14 * max(1.0, np.max(np.abs(base.d_hidden)) * v)
+    np.testing.assert_allclose(aug.d_hidden[:, :h], base.d_hidden, rtol=1e-12, atol=1e-15)
     # a constant vector added to every vocabulary row shifts each row's logits uniformly
     c = rng.standard_normal(h)
     sh = orc.cross_entropy(x, w + c[None, :], t)

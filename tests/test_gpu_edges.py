@@ -74,6 +74,36 @@ def test_zero_weight_closed_form():
     assert rel_max(gpu["d_weight"], expect) <= GRAD_TOL
 
 
+def test_dlogit_rows_sum_to_zero():
+    """Each token's row of dloss/dlogits sums to zero. The last 64 hidden
+    features are 0 in X and 1.0 in every row of W: the logits are unchanged,
+    and each of those dX columns is the token's sum over the vocabulary of
+    dloss/dlogits (G rounded to bf16, as the contractions take it). Checked
+    against the oracle on the same inputs and, explicitly, for being small
+    against the real dX columns."""
+    import torch
+    say("case dlogit row sums")
+    w = BASE.with_dims(name="rowsum", n_tokens=700, hidden=256, vocab=4 * 500, n_shards=4, ignore_frac=0.1,
+                       w_std=0.1)
+    b = workloads.make(w, seed=11)
+    x_bits = np.ascontiguousarray(b.hidden).copy()
+    w_bits = np.ascontiguousarray(b.weight).copy()
+    x_bits[:, -64:] = 0             # bf16 +0.0
+    w_bits[:, -64:] = 0x3F80        # bf16 1.0
+    hidden = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    vs = w.shard_rows
+    shards = [torch.from_numpy(w_bits[s * vs:(s + 1) * vs].view(np.int16)).view(torch.bfloat16).cuda()
+              for s in range(w.n_shards)]
+    targets = torch.from_numpy(np.ascontiguousarray(b.targets, dtype=np.int32)).cuda()
+    gpu = run_lce(hidden, shards, targets)
+    ref = oracle.cross_entropy(oracle.bf16_to_f64(x_bits), oracle.bf16_to_f64(w_bits), b.targets)
+    compare(gpu, ref, "dlogit row sums")
+    assert np.max(np.abs(ref.d_hidden[:, -64:])) <= 1e-12 * np.max(np.abs(ref.d_hidden))  # fp64 rounding only
+    sums = gpu["d_hidden"][:, -64:]
+    assert np.all(sums == sums[:, :1])  # the 64 columns read the same sum
+    assert np.max(np.abs(sums)) <= GRAD_TOL * np.max(np.abs(ref.d_hidden[:, :-64]))
+
+
 def test_ring_order_invariance_and_determinism():
     say("case ring order")
     w = BASE.with_dims(name="order", n_tokens=700, hidden=256, vocab=8 * 300, n_shards=8, ignore_frac=0.1, w_std=0.2)

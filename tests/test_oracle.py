@@ -124,6 +124,7 @@ MUTANTS = {
     "weight row one-hot at the wrong id": ("(t[:, None] == ids[None, :])", "(t[:, None] == ids[None, :] + 1)"),
     "weight row without the normalizer": ("np.exp(z - lse[:, None])", "np.exp(z)"),
     "per-token loss reported as a mean": ('if reduction in ("sum", "none"):', 'if reduction == "sum":'),
+    "softmax with another token's normalizer": ("p = np.exp(z - lse_b[:, None])", "p = np.exp(z - lse_b[::-1, None])"),
 }
 
 
