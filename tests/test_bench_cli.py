@@ -20,5 +20,5 @@ def test_help_lists_the_options():
                        timeout=120)
     assert r.returncode == 0
     for opt in ("--gpus", "--steps", "--warmup", "--workload", "--no-cpu-baseline", "--copy-calibration-mib",
-                "--variants", "--compare-materialized"):
+                "--variants", "--compare-materialized", "--no-power-context"):
         assert opt in r.stdout, opt
