@@ -222,7 +222,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_round_kernel(FwdArgs a, Shard
   for (int i = 0; i < n_all; ++i) {
     const int vt = t0 + i % n_my;
     Acc acc;
-    tile_mainloop<false, false, true, true>(lw, lx, a.H, lds, acc);
+    // a shard's last tile with at most 128 live rows gets its own copy of the
+    // loop, in which the waves of rows 128-255 skip the MFMAs
+    if (__builtin_amdgcn_readfirstlane(a.Vs - vt * kBM <= kWaveM ? 1 : 0))
+      tile_mainloop<false, false, true, true>(lw, lx, a.H, lds, acc, true);
+    else
+      tile_mainloop<false, false, true, true>(lw, lx, a.H, lds, acc);
     if (i + 1 < n_all) {  // the next tile's first stages load while this one folds
       lw.init(shards.p[k_begin + (i + 1) / n_my], a.H, (t0 + (i + 1) % n_my) * kBM, a.Vs, wave, lane);
       tile_prologue(lw, lx, a.H, lds);
